@@ -1,0 +1,433 @@
+// libnhm C ABI: host-side validation, workspace layout and the launch order of
+// the mixer block. Nothing here allocates, caches or synchronizes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "nhm_device.h"
+#include "nhm_internal.h"
+
+namespace nhm {
+
+static thread_local char g_err[512] = "";
+
+nhm_status fail(nhm_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+nhm_status check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(NHM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return NHM_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+static nhm_status check_geometry(const nhm_geometry* g) {
+    if (!g) return fail(NHM_ERR_NULL, "geometry is NULL");
+    if (g->hidden <= 0 || g->n_heads <= 0 || g->n_groups <= 0)
+        return fail(NHM_ERR_UNSUPPORTED, "hidden, n_heads and n_groups must be positive");
+    if (g->head_dim != 64 || g->d_state != 128 || g->conv_width != 4)
+        return fail(NHM_ERR_UNSUPPORTED, "kernels implement head_dim 64, d_state 128, conv_width 4 (got %d, %d, %d)",
+                    g->head_dim, g->d_state, g->conv_width);
+    if (g->n_heads % g->n_groups != 0)
+        return fail(NHM_ERR_UNSUPPORTED, "n_heads %d is not a multiple of n_groups %d", g->n_heads, g->n_groups);
+    if (g->hidden % 16 != 0) return fail(NHM_ERR_UNSUPPORTED, "hidden %d is not a multiple of 16", g->hidden);
+    if (!(g->rms_eps > 0.f) || !isfinite(g->rms_eps))
+        return fail(NHM_ERR_UNSUPPORTED, "rms_eps must be finite and > 0 (got %g)", (double)g->rms_eps);
+    return NHM_OK;
+}
+
+static void fill_layout(const nhm_geometry* g, nhm_layout* l) {
+    const int32_t inner = g->n_heads * g->head_dim;
+    const int32_t gs = g->n_groups * g->d_state;
+    l->d_inner = inner;
+    l->conv_dim = inner + 2 * gs;
+    l->d_in_proj = inner + l->conv_dim + g->n_heads;
+    l->z_off = 0;
+    l->z_width = inner;
+    l->xbc_off = inner;
+    l->xbc_width = l->conv_dim;
+    l->dt_off = inner + l->conv_dim;
+    l->dt_width = g->n_heads;
+    l->x_off = 0;
+    l->x_width = inner;
+    l->b_off = inner;
+    l->b_width = gs;
+    l->c_off = inner + gs;
+    l->c_width = gs;
+    l->heads_per_group = g->n_heads / g->n_groups;
+    l->norm_group = inner / g->n_groups;
+}
+
+static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, const char* name) {
+    if (!w->w || !w->w_scale || !w->a_scale) return fail(NHM_ERR_NULL, "%s: NULL weight, w_scale or a_scale", name);
+    if (w->n != n || w->k != k)
+        return fail(NHM_ERR_SHAPE, "%s: weight is [%lld, %lld], expected [%lld, %lld] ([out, in])", name,
+                    (long long)w->n, (long long)w->k, (long long)n, (long long)k);
+    if (!aligned(w->w, 16) || !aligned(w->w_scale, 4) || !aligned(w->a_scale, 4))
+        return fail(NHM_ERR_ALIGN, "%s: weight must be 16-byte aligned, scales 4-byte aligned", name);
+    return NHM_OK;
+}
+
+// ---------------------------------------------------------------- workspace layouts
+
+struct LinearWs {
+    size_t q, gemv, total;
+};
+static LinearWs linear_ws(int64_t m, int64_t n, int64_t k, nhm_dtype t) {
+    LinearWs l{};
+    size_t off = 0;
+    l.q = off;
+    if (t == NHM_BF16) off += align_up((size_t)m * (size_t)k, 256);
+    l.gemv = off;
+    if (m <= 16) off += gemv_workspace_bytes(m, n, k);
+    l.total = off;
+    return l;
+}
+
+struct MixerWs {
+    nhm_ws_layout pub;
+    size_t gemv_in, gemv_out, group_cnt, chunk_info, seq_chunk0, chunk_cs, chunk_dt, chunk_state;
+    int max_chunks;
+};
+
+static MixerWs decode_ws(const nhm_geometry* g, int32_t batch) {
+    nhm_layout l;
+    fill_layout(g, &l);
+    MixerWs w{};
+    const size_t B = (size_t)batch;
+    const int64_t mg = batch < 16 ? batch : 16;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
+    w.gemv_in = take(gemv_workspace_bytes(mg, l.d_in_proj, g->hidden));
+    w.gemv_out = take(gemv_workspace_bytes(mg, g->hidden, l.d_inner));
+    w.group_cnt = take(B * g->n_groups * sizeof(unsigned));
+    w.pub.q_in = take(B * g->hidden);
+    w.pub.zxbcdt = take(B * l.d_in_proj * 2);
+    w.pub.xbc_conv = take(B * l.conv_dim * 2);
+    w.pub.y = take(B * l.d_inner * 2);
+    w.pub.norm = take(B * l.d_inner * 2);
+    w.pub.q_out = take(B * l.d_inner);
+    w.pub.total = off;
+    return w;
+}
+
+static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t chunk) {
+    nhm_layout l;
+    fill_layout(g, &l);
+    MixerWs w{};
+    const size_t Ts = (size_t)T;
+    const int64_t mg = T < 16 ? T : 16;
+    w.max_chunks = (int)(T / chunk + n);
+    const size_t C = (size_t)w.max_chunks;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
+    w.gemv_in = take(gemv_workspace_bytes(mg, l.d_in_proj, g->hidden));
+    w.gemv_out = take(gemv_workspace_bytes(mg, g->hidden, l.d_inner));
+    w.pub.q_in = take(Ts * g->hidden);
+    w.pub.zxbcdt = take(Ts * l.d_in_proj * 2);
+    w.pub.xbc_conv = take(Ts * l.conv_dim * 2);
+    w.chunk_info = take(C * 4 * sizeof(int32_t));
+    w.seq_chunk0 = take(((size_t)n + 1) * sizeof(int32_t));
+    w.chunk_cs = take(C * g->n_heads * chunk * sizeof(float));
+    w.chunk_dt = take(C * g->n_heads * chunk * sizeof(float));
+    w.chunk_state = take(C * g->n_heads * g->head_dim * g->d_state * sizeof(float));
+    w.pub.y = take(Ts * l.d_inner * 2);
+    w.pub.norm = take(Ts * l.d_inner * 2);
+    w.pub.q_out = take(Ts * l.d_inner);
+    w.pub.total = off;
+    return w;
+}
+
+// One projection of the block on an e4m3 activation: GEMV for m <= 16, else GEMM.
+static nhm_status project(const uint8_t* a, int64_t m, const nhm_fp8_weight& w, uint16_t* out, int64_t ld_out,
+                          const ConvEpilogue* conv, void* gemv_ws, hipStream_t st) {
+    if (m <= 16) return launch_gemv(a, w.k, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, gemv_ws, st);
+    return launch_gemm(a, w.k, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
+}
+
+static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
+    if (!p) return fail(NHM_ERR_NULL, "params is NULL");
+    nhm_status s = check_geometry(&p->g);
+    if (s != NHM_OK) return s;
+    fill_layout(&p->g, l);
+    if ((s = check_weight(&p->in_proj, l->d_in_proj, p->g.hidden, "in_proj")) != NHM_OK) return s;
+    if ((s = check_weight(&p->out_proj, p->g.hidden, l->d_inner, "out_proj")) != NHM_OK) return s;
+    if (!p->conv_w || !p->conv_b || !p->norm_w || !p->A_log || !p->D || !p->dt_bias)
+        return fail(NHM_ERR_NULL, "a block parameter pointer is NULL");
+    if (!aligned(p->conv_w, 16) || !aligned(p->conv_b, 16) || !aligned(p->norm_w, 16) || !aligned(p->A_log, 4) ||
+        !aligned(p->D, 4) || !aligned(p->dt_bias, 4))
+        return fail(NHM_ERR_ALIGN, "conv_w, conv_b and norm_w must be 16-byte aligned, f32 params 4-byte aligned");
+    return NHM_OK;
+}
+
+}  // namespace nhm
+
+using namespace nhm;
+
+extern "C" {
+
+const char* nhm_status_str(nhm_status s) {
+    switch (s) {
+        case NHM_OK: return "NHM_OK";
+        case NHM_ERR_NULL: return "NHM_ERR_NULL";
+        case NHM_ERR_SHAPE: return "NHM_ERR_SHAPE";
+        case NHM_ERR_ALIGN: return "NHM_ERR_ALIGN";
+        case NHM_ERR_UNSUPPORTED: return "NHM_ERR_UNSUPPORTED";
+        case NHM_ERR_WORKSPACE: return "NHM_ERR_WORKSPACE";
+        case NHM_ERR_HIP: return "NHM_ERR_HIP";
+    }
+    return "NHM_ERR_UNKNOWN";
+}
+
+const char* nhm_last_error(void) { return g_err; }
+
+const char* nhm_build_arch(void) { return "gfx950"; }
+
+nhm_status nhm_mixer_layout(const nhm_geometry* g, nhm_layout* out) {
+    g_err[0] = 0;
+    if (!out) return fail(NHM_ERR_NULL, "layout output is NULL");
+    nhm_status s = check_geometry(g);
+    if (s != NHM_OK) return s;
+    fill_layout(g, out);
+    return NHM_OK;
+}
+
+nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
+                                   uint8_t* q, int64_t ld_q, void* stream) {
+    g_err[0] = 0;
+    if (rows < 0 || cols < 0) return fail(NHM_ERR_SHAPE, "negative rows/cols (%lld, %lld)", (long long)rows, (long long)cols);
+    if (rows == 0 || cols == 0) return NHM_OK;
+    if (!x || !scale || !q) return fail(NHM_ERR_NULL, "x, scale or q is NULL");
+    if (ld_x < cols || ld_q < cols)
+        return fail(NHM_ERR_SHAPE, "leading dimensions (%lld, %lld) smaller than cols %lld", (long long)ld_x,
+                    (long long)ld_q, (long long)cols);
+    if (!aligned(x, 2) || !aligned(scale, 4)) return fail(NHM_ERR_ALIGN, "x must be 2-byte, scale 4-byte aligned");
+    launch_quantize(x, rows, cols, ld_x, scale, q, ld_q, (hipStream_t)stream);
+    return check_launch("quantize_static");
+}
+
+size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type) {
+    if (m <= 0 || n <= 0 || k <= 0) return 0;
+    return linear_ws(m, n, k, a_type).total;
+}
+
+nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
+                          uint16_t* out, int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!w) return fail(NHM_ERR_NULL, "weight is NULL");
+    if (a_type != NHM_BF16 && a_type != NHM_E4M3) return fail(NHM_ERR_UNSUPPORTED, "unknown activation dtype %d", (int)a_type);
+    if (m < 0) return fail(NHM_ERR_SHAPE, "negative m");
+    if (w->n <= 0 || w->k <= 0 || w->k % 16 != 0)
+        return fail(NHM_ERR_SHAPE, "weight [%lld, %lld]: n and k must be positive, k a multiple of 16", (long long)w->n,
+                    (long long)w->k);
+    nhm_status s = check_weight(w, w->n, w->k, "weight");
+    if (s != NHM_OK) return s;
+    if (m == 0) return NHM_OK;
+    if (!a || !out) return fail(NHM_ERR_NULL, "a or out is NULL");
+    if (ld_a < w->k || ld_out < w->n)
+        return fail(NHM_ERR_SHAPE, "ld_a %lld < k %lld or ld_out %lld < n %lld", (long long)ld_a, (long long)w->k,
+                    (long long)ld_out, (long long)w->n);
+    if (!aligned(a, 16) || (a_type == NHM_BF16 ? ld_a % 8 : ld_a % 16) != 0)
+        return fail(NHM_ERR_ALIGN, "a must be 16-byte aligned with 16-byte row stride");
+    if (!aligned(out, 2)) return fail(NHM_ERR_ALIGN, "out must be 2-byte aligned");
+    const LinearWs l = linear_ws(m, w->n, w->k, a_type);
+    if (l.total > 0 && (!ws || ws_bytes < l.total))
+        return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", l.total, ws ? ws_bytes : (size_t)0);
+    if (ws && !aligned(ws, 256)) return fail(NHM_ERR_ALIGN, "ws must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* aq = static_cast<const uint8_t*>(a);
+    int64_t lda = ld_a;
+    char* wsb = static_cast<char*>(ws);
+    if (a_type == NHM_BF16) {
+        uint8_t* q = reinterpret_cast<uint8_t*>(wsb + l.q);
+        launch_quantize(static_cast<const uint16_t*>(a), m, w->k, ld_a, w->a_scale, q, w->k, st);
+        if ((s = check_launch("quantize_static")) != NHM_OK) return s;
+        aq = q;
+        lda = w->k;
+    }
+    if (m <= 16)
+        return launch_gemv(aq, lda, (int)m, w->w, w->w_scale, w->a_scale, w->n, w->k, out, ld_out, nullptr,
+                           wsb + l.gemv, st);
+    return launch_gemm(aq, lda, m, w->w, w->w_scale, w->a_scale, w->n, w->k, out, ld_out, st);
+}
+
+nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
+    g_err[0] = 0;
+    if (!out) return fail(NHM_ERR_NULL, "layout output is NULL");
+    nhm_status s = check_geometry(g);
+    if (s != NHM_OK) return s;
+    if (batch < 0) return fail(NHM_ERR_SHAPE, "negative batch");
+    *out = decode_ws(g, batch).pub;
+    return NHM_OK;
+}
+
+nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_tokens, int32_t n_seqs, int32_t chunk,
+                                       nhm_ws_layout* out) {
+    g_err[0] = 0;
+    if (!out) return fail(NHM_ERR_NULL, "layout output is NULL");
+    nhm_status s = check_geometry(g);
+    if (s != NHM_OK) return s;
+    if (chunk != 128) return fail(NHM_ERR_UNSUPPORTED, "chunk %d: this build implements chunk 128", chunk);
+    if (n_tokens < 0 || n_seqs < 0 || n_tokens > INT32_MAX)
+        return fail(NHM_ERR_SHAPE, "n_tokens %lld / n_seqs %d out of range", (long long)n_tokens, n_seqs);
+    *out = prefill_ws(g, n_tokens, n_seqs, chunk).pub;
+    return NHM_OK;
+}
+
+nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch, const int32_t* slot_idx,
+                            float* ssm_pool, uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    nhm_layout l;
+    nhm_status s = check_params(p, &l);
+    if (s != NHM_OK) return s;
+    if (batch < 0) return fail(NHM_ERR_SHAPE, "negative batch");
+    if (batch == 0) return NHM_OK;
+    if (n_slots <= 0) return fail(NHM_ERR_SHAPE, "n_slots must be positive");
+    if (!hidden || !slot_idx || !ssm_pool || !conv_pool || !out || !ws)
+        return fail(NHM_ERR_NULL, "hidden, slot_idx, pools, out or ws is NULL");
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
+        !aligned(slot_idx, 4) || !aligned(ws, 256))
+        return fail(NHM_ERR_ALIGN, "hidden, out and pools must be 16-byte aligned, ws 256-byte aligned");
+    const MixerWs w = decode_ws(&p->g, batch);
+    if (ws_bytes < w.pub.total)
+        return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    char* wsb = static_cast<char*>(ws);
+    const int64_t H = p->g.hidden;
+    uint8_t* q_in = reinterpret_cast<uint8_t*>(wsb + w.pub.q_in);
+    uint16_t* zx = reinterpret_cast<uint16_t*>(wsb + w.pub.zxbcdt);
+    uint16_t* xc = reinterpret_cast<uint16_t*>(wsb + w.pub.xbc_conv);
+    uint8_t* q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
+
+    launch_quantize(hidden, batch, H, H, p->in_proj.a_scale, q_in, H, st);
+    if ((s = check_launch("decode quant")) != NHM_OK) return s;
+    for (int32_t r0 = 0; r0 < batch; r0 += 16) {
+        const int mg = batch - r0 < 16 ? batch - r0 : 16;
+        ConvEpilogue ce{slot_idx + r0, conv_pool, p->conv_w, p->conv_b, xc + (int64_t)r0 * l.conv_dim, l.xbc_off,
+                        l.conv_dim};
+        s = project(q_in + (int64_t)r0 * H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce,
+                    wsb + w.gemv_in, st);
+        if (s != NHM_OK) return s;
+    }
+    DecodeSsmArgs da;
+    da.slot_idx = slot_idx;
+    da.ssm_pool = ssm_pool;
+    da.zxbcdt = zx;
+    da.xbc_conv = xc;
+    da.A_log = p->A_log;
+    da.D = p->D;
+    da.dt_bias = p->dt_bias;
+    da.norm_w = p->norm_w;
+    da.out_a_scale = p->out_proj.a_scale;
+    da.y = reinterpret_cast<uint16_t*>(wsb + w.pub.y);
+    da.norm = reinterpret_cast<uint16_t*>(wsb + w.pub.norm);
+    da.q_out = q_out;
+    da.group_counters = reinterpret_cast<unsigned*>(wsb + w.group_cnt);
+    da.n_heads = p->g.n_heads;
+    da.n_groups = p->g.n_groups;
+    da.d_in_proj = l.d_in_proj;
+    da.conv_dim = l.conv_dim;
+    da.d_inner = l.d_inner;
+    da.z_off = l.z_off;
+    da.dt_off = l.dt_off;
+    da.b_off = l.b_off;
+    da.c_off = l.c_off;
+    da.eps = p->g.rms_eps;
+    if ((s = launch_decode_ssm(da, batch, st)) != NHM_OK) return s;
+    for (int32_t r0 = 0; r0 < batch; r0 += 16) {
+        const int mg = batch - r0 < 16 ? batch - r0 : 16;
+        s = project(q_out + (int64_t)r0 * l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, nullptr,
+                    wsb + w.gemv_out, st);
+        if (s != NHM_OK) return s;
+    }
+    return NHM_OK;
+}
+
+nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,
+                             const int32_t* cu_seqlens, int32_t n_seqs, const int32_t* slot_idx,
+                             const int32_t* has_initial, int32_t chunk, float* ssm_pool, uint16_t* conv_pool,
+                             int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    nhm_layout l;
+    nhm_status s = check_params(p, &l);
+    if (s != NHM_OK) return s;
+    if (chunk != 128) return fail(NHM_ERR_UNSUPPORTED, "chunk %d: this build implements chunk 128", chunk);
+    if (n_tokens < 0 || n_seqs < 0 || n_tokens > INT32_MAX)
+        return fail(NHM_ERR_SHAPE, "n_tokens %lld / n_seqs %d out of range", (long long)n_tokens, n_seqs);
+    if (n_seqs == 0) {
+        if (n_tokens != 0) return fail(NHM_ERR_SHAPE, "%lld tokens but no sequences", (long long)n_tokens);
+        return NHM_OK;
+    }
+    if (n_slots <= 0) return fail(NHM_ERR_SHAPE, "n_slots must be positive");
+    if (n_seqs > n_slots) return fail(NHM_ERR_SHAPE, "%d sequences need distinct slots, pool has %d", n_seqs, n_slots);
+    if (!cu_seqlens || !slot_idx || !has_initial || !ssm_pool || !conv_pool || !ws || (n_tokens > 0 && (!hidden || !out)))
+        return fail(NHM_ERR_NULL, "a required pointer is NULL");
+    if ((hidden && !aligned(hidden, 16)) || (out && !aligned(out, 16)) || !aligned(ssm_pool, 16) ||
+        !aligned(conv_pool, 16) || !aligned(cu_seqlens, 4) || !aligned(slot_idx, 4) || !aligned(has_initial, 4) ||
+        !aligned(ws, 256))
+        return fail(NHM_ERR_ALIGN, "hidden, out and pools must be 16-byte aligned, ws 256-byte aligned");
+    const MixerWs w = prefill_ws(&p->g, n_tokens, n_seqs, chunk);
+    if (ws_bytes < w.pub.total)
+        return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    char* wsb = static_cast<char*>(ws);
+    const int64_t H = p->g.hidden;
+    uint8_t* q_in = reinterpret_cast<uint8_t*>(wsb + w.pub.q_in);
+    uint16_t* zx = reinterpret_cast<uint16_t*>(wsb + w.pub.zxbcdt);
+    if (n_tokens > 0) {
+        launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
+        if ((s = check_launch("prefill quant")) != NHM_OK) return s;
+        if ((s = project(q_in, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, wsb + w.gemv_in, st)) != NHM_OK) return s;
+    }
+    PrefillArgs a;
+    a.T = n_tokens;
+    a.n_seqs = n_seqs;
+    a.chunk = chunk;
+    a.max_chunks = w.max_chunks;
+    a.n_heads = p->g.n_heads;
+    a.n_groups = p->g.n_groups;
+    a.d_in_proj = l.d_in_proj;
+    a.conv_dim = l.conv_dim;
+    a.d_inner = l.d_inner;
+    a.z_off = l.z_off;
+    a.xbc_off = l.xbc_off;
+    a.dt_off = l.dt_off;
+    a.b_off = l.b_off;
+    a.c_off = l.c_off;
+    a.eps = p->g.rms_eps;
+    a.cu_seqlens = cu_seqlens;
+    a.slot_idx = slot_idx;
+    a.has_initial = has_initial;
+    a.ssm_pool = ssm_pool;
+    a.conv_pool = conv_pool;
+    a.conv_w = p->conv_w;
+    a.conv_b = p->conv_b;
+    a.A_log = p->A_log;
+    a.D = p->D;
+    a.dt_bias = p->dt_bias;
+    a.norm_w = p->norm_w;
+    a.out_a_scale = p->out_proj.a_scale;
+    a.zxbcdt = zx;
+    a.xbc_conv = reinterpret_cast<uint16_t*>(wsb + w.pub.xbc_conv);
+    a.chunk_info = reinterpret_cast<int32_t*>(wsb + w.chunk_info);
+    a.seq_chunk0 = reinterpret_cast<int32_t*>(wsb + w.seq_chunk0);
+    a.chunk_cs = reinterpret_cast<float*>(wsb + w.chunk_cs);
+    a.chunk_dt = reinterpret_cast<float*>(wsb + w.chunk_dt);
+    a.chunk_state = reinterpret_cast<float*>(wsb + w.chunk_state);
+    a.y = reinterpret_cast<uint16_t*>(wsb + w.pub.y);
+    a.norm = reinterpret_cast<uint16_t*>(wsb + w.pub.norm);
+    a.q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
+    if ((s = launch_prefill_mid(a, st)) != NHM_OK) return s;
+    if (n_tokens > 0)
+        return project(a.q_out, n_tokens, p->out_proj, out, H, nullptr, wsb + w.gemv_out, st);
+    return NHM_OK;
+}
+
+}  // extern "C"

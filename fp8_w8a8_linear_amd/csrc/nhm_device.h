@@ -1,0 +1,77 @@
+// Device-side number formats and small helpers shared by the libnhm kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nhm {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16 bits, round half to even; NaN becomes a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// float -> OCP FP8 E4M3FN code: round half to even, saturating at +-448 (infinities
+// included), NaN -> 0x7F with the sign kept, zero results keep the sign bit.
+// Integer form: for |v| in [2^-6, 448) the code is the float's biased exponent and
+// top three mantissa bits, rounded half to even on the 20 bits below them and
+// re-biased from 127 to 7; below 2^-6 the code counts multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t s = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t c;
+    if (a > 0x7f800000u) {
+        c = 0x7fu;
+    } else if (a >= 0x43e00000u) {          // 448.0f
+        c = 0x7eu;
+    } else if (a < 0x3c800000u) {           // 2^-6
+        c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    } else {
+        c = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    }
+    return s | c;
+}
+
+// Exact float value of an e4m3 code (finite codes; the GEMMs never decode in software).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// The static activation quant of one bf16 value: E4M3(f32(x) / s), IEEE division.
+__device__ __forceinline__ uint32_t quant_bf16(uint32_t xb, float s) {
+    return e4m3_code(__fdiv_rn(bf16_to_f32(xb), s));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(__expf(u)); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// 16x16x128 e4m3 MFMA, f32 accumulate (gfx950). Lane l supplies row (l % 16) of A
+// and column (l % 16) of B, each as 32 consecutive k-bytes of the 128-k step chosen
+// by l / 16; the accumulator lane l, register r holds D[4*(l/16)+r][l%16].
+__device__ __forceinline__ v4f mfma_e4m3(const v8i& a, const v8i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+}  // namespace nhm

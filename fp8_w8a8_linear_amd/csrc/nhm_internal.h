@@ -1,0 +1,109 @@
+// Host-side declarations shared by the libnhm translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nhm.h"
+
+namespace nhm {
+
+// Records a failure detail for nhm_last_error() and returns the status.
+nhm_status fail(nhm_status s, const char* fmt, ...);
+
+// Returns NHM_ERR_HIP (with the runtime's message) if the last launch failed.
+nhm_status check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- activation quant (quant.hip)
+void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
+                     uint8_t* q, int64_t ld_q, hipStream_t st);
+
+// ---- weight-streaming GEMV for m <= 16 (gemv.hip)
+struct GemvPlan {
+    int row_blocks;     // ceil(n / 64)
+    int ksteps;         // ceil(k / 128)
+    int steps_per_split;
+    int ksplit;
+};
+GemvPlan gemv_plan(int64_t n, int64_t k);
+size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k);   // partials + counters
+
+// Epilogue of the in_proj GEMV inside a decode step: besides storing the bf16
+// projection, runs the causal conv + SiLU on the xBC columns and shifts the
+// carried conv window of each sequence in place.
+struct ConvEpilogue {
+    const int32_t* slot_idx;   // [m]
+    uint16_t* conv_pool;       // [S, W-1, conv_dim]
+    const uint16_t* conv_w;    // [conv_dim, W]
+    const uint16_t* conv_b;    // [conv_dim]
+    uint16_t* xbc_conv;        // [m, conv_dim]
+    int32_t xbc_off;           // first xBC column of the projection
+    int32_t conv_dim;
+};
+
+// out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda].
+// conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue.
+nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
+                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
+                       const ConvEpilogue* conv, void* ws, hipStream_t st);
+
+// ---- tiled MFMA GEMM for larger m (gemm.hip)
+nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
+                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
+                       hipStream_t st);
+
+// ---- decode SSM update + gated group RMSNorm + out_proj quant (decode.hip)
+struct DecodeSsmArgs {
+    const int32_t* slot_idx;
+    float* ssm_pool;
+    const uint16_t* zxbcdt;    // [m, d_in_proj]
+    const uint16_t* xbc_conv;  // [m, conv_dim]
+    const float* A_log;
+    const float* D;
+    const float* dt_bias;
+    const uint16_t* norm_w;
+    const float* out_a_scale;
+    uint16_t* y;               // [m, d_inner]
+    uint16_t* norm;            // [m, d_inner]
+    uint8_t* q_out;            // [m, d_inner]
+    unsigned* group_counters;  // [m * n_groups], zero between calls
+    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, z_off, dt_off, b_off, c_off;
+    float eps;
+};
+nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st);
+
+// ---- prefill pieces (prefill.hip)
+struct PrefillArgs {
+    int64_t T;
+    int32_t n_seqs, chunk, max_chunks, n_heads, n_groups, d_in_proj, conv_dim, d_inner;
+    int32_t z_off, xbc_off, dt_off, b_off, c_off;
+    float eps;
+    const int32_t* cu_seqlens;
+    const int32_t* slot_idx;
+    const int32_t* has_initial;
+    float* ssm_pool;
+    uint16_t* conv_pool;
+    const uint16_t* conv_w;
+    const uint16_t* conv_b;
+    const float* A_log;
+    const float* D;
+    const float* dt_bias;
+    const uint16_t* norm_w;
+    const float* out_a_scale;
+    const uint16_t* zxbcdt;   // [T, d_in_proj]
+    uint16_t* xbc_conv;       // [T, conv_dim]
+    int32_t* chunk_info;      // [max_chunks, 4]: seq, tok0, len, index in seq
+    int32_t* seq_chunk0;      // [n_seqs + 1]
+    float* chunk_cs;          // [max_chunks, n_heads, chunk]  cumulative log-decay
+    float* chunk_dt;          // [max_chunks, n_heads, chunk]
+    float* chunk_state;       // [max_chunks, n_heads, 64, 128]
+    uint16_t* y;              // [T, d_inner]
+    uint16_t* norm;           // [T, d_inner] (nullptr: not kept)
+    uint8_t* q_out;           // [T, d_inner]
+};
+nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace nhm

@@ -1,0 +1,259 @@
+/*
+ * nhm.h -- C ABI of libnhm: the NemotronH Mamba2 mixer with FP8 W8A8 projections
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (pull-request pages of one C++ LLM inference project, cited by number):
+ *   [PR1288] "feat(#810 A2-Q1): NemotronH's 23 Mamba2 blocks reach the device on the
+ *            FP8 W8A8 seam (#517)"
+ *   [PR1289] the same change re-filed as #1289 (conversation and commit log)
+ *   [PR988]  "spec(#810 A2-Q): split the quantized arms into A2-Q1 and A2-Q2, because
+ *            their blockers differ (#517)"
+ *   [PR950]  "feat(#810 A2-R): NemotronH's dense weights reach the device, and the
+ *            attention block that reads them is model-local (#517)"
+ *   [PR972]  "refactor(VT-FP8-SHARED-SEAM): the FP8 W8A8 linear path becomes a seam a
+ *            second model can reach (#940)"
+ *
+ * Conventions that hold for every entry point:
+ *   - Pointers marked (device) address GPU memory; (host) address host memory.
+ *     The caller owns every buffer. The library allocates nothing, keeps no cache and
+ *     no state between calls, never synchronizes the device, and only enqueues work
+ *     on the given stream (a hipStream_t; NULL = the default stream). All calls are
+ *     therefore legal inside HIP graph capture.
+ *   - Shapes, null pointers, alignment and geometry are validated on the host before
+ *     anything is enqueued. A failed check returns a status and enqueues nothing; no
+ *     C++ exception crosses the ABI. nhm_last_error() then describes the failure.
+ *   - A failed kernel launch returns NHM_ERR_HIP.
+ *   - Values that live only on the device (slot indices, cu_seqlens, has_initial)
+ *     cannot be checked without a synchronization; their contract is stated per call
+ *     and violating it is undefined behaviour.
+ *   - bf16 tensors are passed as uint16_t bit patterns, e4m3 tensors as uint8_t
+ *     codes (OCP FP8 E4M3FN: largest finite 448, no infinities).
+ *   - Workspaces ("ws") are caller-allocated device memory that MUST be zero-filled
+ *     once when allocated. Every call leaves the workspace's synchronisation counters
+ *     at zero again, so later calls need no clearing. One workspace must not be used
+ *     by two calls that can run at the same time (e.g. on two streams).
+ */
+#ifndef NHM_H
+#define NHM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define NHM_API __attribute__((visibility("default")))
+#else
+#define NHM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+
+typedef enum nhm_status {
+    NHM_OK = 0,
+    NHM_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    NHM_ERR_SHAPE = 2,       /* a size or leading dimension is out of range        */
+    NHM_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned       */
+    NHM_ERR_UNSUPPORTED = 4, /* a geometry or option this build does not implement */
+    NHM_ERR_WORKSPACE = 5,   /* ws is NULL or smaller than the call needs          */
+    NHM_ERR_HIP = 6          /* the HIP runtime reported an error                  */
+} nhm_status;
+
+typedef enum nhm_dtype {
+    NHM_BF16 = 0,            /* bfloat16 bit patterns (uint16_t)                   */
+    NHM_E4M3 = 1             /* OCP FP8 E4M3FN codes (uint8_t)                      */
+} nhm_dtype;
+
+/* Static name of a status code. Never NULL. */
+NHM_API const char* nhm_status_str(nhm_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). The string stays
+ * valid until the next libnhm call on the same thread. */
+NHM_API const char* nhm_last_error(void);
+
+/* Name of the GPU architecture the library was built for ("gfx950"). */
+NHM_API const char* nhm_build_arch(void);
+
+/* ---------------------------------------------------------------- geometry */
+
+/* Mixer geometry. [PR1288] opening section (2688 -> 10304 in_proj, 4096 -> 2688
+ * out_proj); [PR950] "Review repairs" F2 (64 heads; three f32 per-head SSM
+ * tensors). Supported by the kernels: head_dim == 64, d_state == 128,
+ * conv_width == 4, n_heads % n_groups == 0, hidden % 16 == 0, 0 < rms_eps
+ * (an eps of 0 is refused: [PR950] "Not dense_attn::AttnBlock (#941)" reports a
+ * missing rms eps key silently becoming 0). */
+typedef struct nhm_geometry {
+    int32_t hidden;      /* model width H (2688)                        */
+    int32_t n_heads;     /* SSM heads (64)                              */
+    int32_t head_dim;    /* P, channels per head (64)                   */
+    int32_t d_state;     /* N, state width per head channel (128)       */
+    int32_t n_groups;    /* G, groups sharing B and C; norm groups (8)  */
+    int32_t conv_width;  /* causal conv taps (4)                        */
+    float rms_eps;       /* gated RMSNorm epsilon (1e-5), > 0           */
+} nhm_geometry;
+
+/* Split indices of one in_proj row and of the conv output.
+ * [PR1289] commit log: the first split has three outputs of widths
+ * (I, conv_dim, num_heads) taking the head, middle and tail of an in_proj row;
+ * [PR1288] "What it does": the second split is x | B | C. */
+typedef struct nhm_layout {
+    int32_t d_inner;          /* I = n_heads * head_dim                      */
+    int32_t conv_dim;         /* I + 2 * n_groups * d_state                  */
+    int32_t d_in_proj;        /* I + conv_dim + n_heads                      */
+    int32_t z_off, z_width;   /* within an in_proj row                       */
+    int32_t xbc_off, xbc_width;
+    int32_t dt_off, dt_width;
+    int32_t x_off, x_width;   /* within an xBC row                           */
+    int32_t b_off, b_width;
+    int32_t c_off, c_width;
+    int32_t heads_per_group;  /* head h reads B/C group h / heads_per_group  */
+    int32_t norm_group;       /* channels per RMSNorm group = I / n_groups   */
+} nhm_layout;
+
+/* Fills *out (host) from *g (host). The kernels index with the same numbers.
+ * Errors: NHM_ERR_NULL, NHM_ERR_UNSUPPORTED (geometry outside the list above). */
+NHM_API nhm_status nhm_mixer_layout(const nhm_geometry* g, nhm_layout* out);
+
+/* ---------------------------------------------------------------- FP8 W8A8 linear */
+
+/* One FP8 W8A8 projection: e4m3 weight in the [out, in] torch-Linear orientation
+ * (row-major [n, k]; [PR950] "Review repairs" F2: the GEMM consumers refuse any
+ * other orientation), an f32 scale per output channel, and the static per-tensor
+ * f32 activation scale ("input_scale"). All three pointers are device memory. */
+typedef struct nhm_fp8_weight {
+    const uint8_t* w;         /* (device) e4m3 [n, k], row stride k, 16-B aligned */
+    const float* w_scale;     /* (device) f32 [n]                                 */
+    const float* a_scale;     /* (device) f32 [1]                                 */
+    int64_t n;                /* output features                                  */
+    int64_t k;                /* input features, k % 16 == 0                      */
+} nhm_fp8_weight;
+
+/* Static per-tensor activation quant: q[r, c] = E4M3(f32(x[r, c]) / scale[0]),
+ * the f32 quotient correctly rounded, the code rounded half to even and saturated
+ * at +-448 (NaN -> 0x7F with the sign kept).
+ * [PR988] "The Thor finding, measured" (the quant op is its own kernel, kQuantFp8Static);
+ * [PR1288] "The comparison is not bit-comparable, and that is the point" (W8A8
+ * applies input_scale to the activation).
+ *   x      (device) bf16 [rows, ld_x], ld_x >= cols
+ *   scale  (device) f32 [1]
+ *   q      (device) e4m3 [rows, ld_q], ld_q >= cols; must not overlap x
+ * rows == 0 or cols == 0 is a valid no-op.
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE (negative sizes, ld < cols), NHM_ERR_ALIGN
+ * (x not 2-byte aligned), NHM_ERR_HIP. */
+NHM_API nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   const float* scale, uint8_t* q, int64_t ld_q, void* stream);
+
+/* Workspace bytes nhm_fp8_linear needs for this shape and input type. */
+NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type);
+
+/* out[i, j] = bf16( (sum_k val(a_q[i, k]) * val(w[j, k])) * a_scale * w_scale[j] ),
+ * accumulated in f32. a_q is a itself when a_type == NHM_E4M3 (a pre-quantized
+ * activation: [PR972] "Correspondence with dense_nvfp4_gemm.h", the
+ * QuantizedActivation overload), else nhm_fp8_quantize_static(a, w->a_scale).
+ * [PR988] "The Thor finding, measured" (e4m3 x e4m3, f32 compute and scale, bf16 D).
+ *   a      (device) [m, ld_a] of a_type, 16-B aligned, ld_a >= k, ld_a % 8 == 0
+ *          (bf16) or % 16 == 0 (e4m3)
+ *   w      (host struct of device pointers)
+ *   out    (device) bf16 [m, ld_out], ld_out >= n; must not overlap a (rows that
+ *          are 8-byte aligned are stored 4 features at a time)
+ *   ws     (device, zero-filled once) >= nhm_fp8_linear_workspace_bytes(m, n, k, a_type)
+ * m == 0 is a valid no-op. m <= 16 runs the weight-streaming GEMV, larger m the
+ * tiled MFMA GEMM. Results are deterministic (no float atomics).
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
+NHM_API nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
+                          const nhm_fp8_weight* w, uint16_t* out, int64_t ld_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- the mixer block */
+
+/* All parameters of one mixer block (device pointers; the struct itself is host).
+ * [PR1288] "What it does": in_proj (FP8 W8A8) -> split z | xBC | dt ->
+ * CausalConv1dFwd(silu) -> split x | B | C -> Mamba2ChunkScan ->
+ * RmsNormGatedGroup(n_groups) -> out_proj (FP8 W8A8). */
+typedef struct nhm_mixer_params {
+    nhm_geometry g;
+    nhm_fp8_weight in_proj;   /* n = d_in_proj, k = hidden   */
+    nhm_fp8_weight out_proj;  /* n = hidden,    k = d_inner  */
+    const uint16_t* conv_w;   /* bf16 [conv_dim, conv_width] */
+    const uint16_t* conv_b;   /* bf16 [conv_dim]             */
+    const uint16_t* norm_w;   /* bf16 [d_inner]              */
+    const float* A_log;       /* f32 [n_heads]; A = -exp(A_log) */
+    const float* D;           /* f32 [n_heads] skip weight   */
+    const float* dt_bias;     /* f32 [n_heads]; dt = softplus(dt_raw + dt_bias) */
+} nhm_mixer_params;
+
+/* Byte offsets of the intermediates a call leaves in its workspace (for
+ * inspection; SIZE_MAX when that call does not keep one), and the total size. */
+typedef struct nhm_ws_layout {
+    size_t total;      /* bytes the call needs                                  */
+    size_t q_in;       /* e4m3 [tokens, hidden]      quantized block input      */
+    size_t zxbcdt;     /* bf16 [tokens, d_in_proj]   in_proj output             */
+    size_t xbc_conv;   /* bf16 [tokens, conv_dim]    conv + SiLU output         */
+    size_t y;          /* bf16 [tokens, d_inner]     SSM output incl. D skip    */
+    size_t norm;       /* bf16 [tokens, d_inner]     gated RMSNorm output       */
+    size_t q_out;      /* e4m3 [tokens, d_inner]     quantized out_proj input   */
+} nhm_ws_layout;
+
+/* Workspace layout of nhm_mixer_decode for `batch` rows.
+ * Errors: NHM_ERR_NULL, NHM_ERR_UNSUPPORTED, NHM_ERR_SHAPE (batch < 0). */
+NHM_API nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out);
+
+/* One decode token for each of `batch` sequences whose recurrent state lives in
+ * pool rows addressed by slot ([PR1288] "What it does": the paged arm hands the
+ * mixer gathered recurrent rows and it advances them IN PLACE; decode always
+ * continues from the stored rows, has_initial = true).
+ *   hidden    (device) bf16 [batch, g.hidden], row stride g.hidden
+ *   slot_idx  (device) int32 [batch]: pool row of each sequence. Contract: every
+ *             non-negative entry is < n_slots and distinct; a negative entry marks
+ *             a padded row, whose output row is zero and which touches no state.
+ *   ssm_pool  (device) f32 [n_slots, n_heads, head_dim, d_state], updated in place
+ *   conv_pool (device) bf16 [n_slots, conv_width-1, conv_dim], the previous
+ *             conv_width-1 pre-conv xBC rows, oldest first; updated in place
+ *   out       (device) bf16 [batch, g.hidden]; must not overlap hidden
+ *   ws        (device, zero-filled once) >= nhm_mixer_decode_ws_layout(...).total
+ * batch == 0 is a valid no-op.
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
+ * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
+NHM_API nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                            const int32_t* slot_idx, float* ssm_pool, uint16_t* conv_pool,
+                            int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace layout of nhm_mixer_prefill for up to n_tokens tokens in up to n_seqs
+ * sequences with SSD chunk length `chunk`.
+ * Errors: NHM_ERR_NULL, NHM_ERR_UNSUPPORTED, NHM_ERR_SHAPE. */
+NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_tokens, int32_t n_seqs,
+                                       int32_t chunk, nhm_ws_layout* out);
+
+/* Varlen prefill of n_seqs packed sequences: sequence i owns tokens
+ * cu_seqlens[i] .. cu_seqlens[i+1]-1 of `hidden`. The Mamba2 chunk scan runs with
+ * chunks of `chunk` tokens that start at each sequence's first token.
+ *   hidden      (device) bf16 [n_tokens, g.hidden]
+ *   cu_seqlens  (device) int32 [n_seqs+1]. Contract: cu_seqlens[0] == 0,
+ *               non-decreasing, cu_seqlens[n_seqs] == n_tokens.
+ *   slot_idx    (device) int32 [n_seqs]. Contract: distinct, in [0, n_slots).
+ *   has_initial (device) int32 [n_seqs]: 0 starts sequence i from zero SSM state and
+ *               a zero conv window; non-zero continues from pool row slot_idx[i].
+ *   chunk       SSD chunk length; this build supports 128.
+ *   ssm_pool, conv_pool: as for nhm_mixer_decode. The final state and window of
+ *               every sequence are written to its row in place (an empty fresh
+ *               sequence leaves a zero row).
+ *   out         (device) bf16 [n_tokens, g.hidden]; must not overlap hidden
+ *   ws          (device, zero-filled once) >=
+ *               nhm_mixer_prefill_ws_layout(g, n_tokens, n_seqs, chunk).total
+ * n_tokens == 0 with n_seqs == 0 is a valid no-op.
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
+ * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
+NHM_API nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,
+                             const int32_t* cu_seqlens, int32_t n_seqs, const int32_t* slot_idx,
+                             const int32_t* has_initial, int32_t chunk, float* ssm_pool,
+                             uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NHM_H */

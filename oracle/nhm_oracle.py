@@ -414,22 +414,42 @@ def mixer_decode(p, hidden_bf16, slot_idx, ssm_pool, conv_pool, g=GEOMETRY):
     [S, H, P, N] float32 and conv_pool: [S, W-1, conv_dim] bf16 are updated IN
     PLACE (copies are the caller's business). Decode always continues from the
     pool rows ([PR1288] "What it does": the paged arm advances gathered rows in
-    place with has_initial = true). Returns (out float64 [B, hidden], list of
-    per-row result dicts).
+    place with has_initial = true). The rows are independent; the two
+    projections are done for all rows at once (same arithmetic as row by row).
+    Returns (out float64 [B, hidden], dict of per-row intermediates).
     """
+    lay = layout(g)
+    H, P, N, G = g["n_heads"], g["head_dim"], g["d_state"], g["n_groups"]
     B = hidden_bf16.shape[0]
+    live = [b for b in range(B) if int(slot_idx[b]) >= 0]
     out = np.zeros((B, g["hidden"]), dtype=np.float64)
-    res = []
-    for b in range(B):
+    res = dict(q_in=quantize_static(hidden_bf16, p["in_a_scale"]))
+    zx = bf16_from_f64(fp8_linear(res["q_in"], p["in_w"], p["in_w_scale"], p["in_a_scale"]))   # a1, a2
+    res["zxbcdt"] = zx
+    xbc_conv = np.zeros((B, lay["conv_dim"]), dtype=np.uint16)
+    y_bf16 = np.zeros((B, lay["d_inner"]), dtype=np.uint16)
+    y64 = np.zeros((B, lay["d_inner"]), dtype=np.float64)
+    for b in live:
         s = int(slot_idx[b])
-        if s < 0:
-            res.append(None)
-            continue
-        r = mixer_sequence(p, hidden_bf16[b:b + 1], conv_pool[s], ssm_pool[s], g)
-        ssm_pool[s] = r["state"]
-        conv_pool[s] = r["window"]
-        out[b] = r["out"][0]
-        res.append(r)
+        z = zx[b:b + 1, lay["z_off"]:lay["z_off"] + lay["z_width"]]
+        xbc = zx[b:b + 1, lay["xbc_off"]:lay["xbc_off"] + lay["xbc_width"]]
+        dt_raw = zx[b:b + 1, lay["dt_off"]:lay["dt_off"] + lay["dt_width"]]
+        _, xc, conv_pool[s] = causal_conv1d_silu(xbc, conv_pool[s], p["conv_w"], p["conv_b"])   # a4
+        xbc_conv[b] = xc[0]
+        xv = bf16_to_f64(xc[:, lay["x_off"]:lay["x_off"] + lay["x_width"]]).reshape(1, H, P)   # a5
+        Bv = bf16_to_f64(xc[:, lay["b_off"]:lay["b_off"] + lay["b_width"]]).reshape(1, G, N)
+        Cv = bf16_to_f64(xc[:, lay["c_off"]:lay["c_off"] + lay["c_width"]]).reshape(1, G, N)
+        dt, dA = dt_and_decay(dt_raw, p["dt_bias"], p["A_log"])                                # a6
+        y, h = ssm_scan_sequential(xv, Bv, Cv, dt, dA, p["D"], ssm_pool[s].astype(np.float64))  # a7
+        ssm_pool[s] = h.astype(np.float32)
+        y64[b] = y.reshape(-1)
+        y_bf16[b] = bf16_from_f64(y.reshape(-1))
+    _, o_bf16 = gated_group_rmsnorm(y_bf16, zx[:, lay["z_off"]:lay["z_off"] + lay["z_width"]],
+                                    p["norm_w"], G, g["rms_eps"])                                # a8
+    q_out = quantize_static(o_bf16, p["out_a_scale"])                                           # a9
+    o = fp8_linear(q_out, p["out_w"], p["out_w_scale"], p["out_a_scale"])                       # a10
+    out[live] = o[live]
+    res.update(xbc_conv=xbc_conv, y=y64, y_bf16=y_bf16, norm_bf16=o_bf16, q_out=q_out)
     return out, res
 
 

@@ -1,0 +1,154 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+refuses bad arguments on the host before anything is enqueued (no GPU needed:
+every call here fails validation before a launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nhm.h")
+
+
+@pytest.fixture(scope="module")
+def nhm():
+    import fp8_w8a8_linear_amd as m
+    return m
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"NHM_API\s+[\w\s\*]+?\b(nhm_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(nhm):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(nhm.lib, n), f"{n} not exported"
+
+
+def test_build_arch(nhm):
+    assert nhm.lib.nhm_build_arch() == b"gfx950"
+    assert nhm.lib.nhm_status_str(4) == b"NHM_ERR_UNSUPPORTED"
+
+
+def test_layout_matches_oracle(nhm):
+    from oracle import layout
+    assert nhm.mixer_layout() == layout()
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 32), ("d_state", 64), ("conv_width", 3), ("n_groups", 7),
+                                         ("rms_eps", 0.0), ("hidden", 100), ("n_heads", 0)])
+def test_unsupported_geometry(nhm, field, value):
+    g = dict(nhm.GEOMETRY)
+    g[field] = value
+    with pytest.raises(nhm.NhmError) as e:
+        nhm.mixer_layout(g)
+    assert e.value.status == 4
+
+
+def _w(nhm, w=0x1000, s=0x2000, a=0x3000, n=64, k=128):
+    return nhm._Fp8Weight(w, s, a, n, k)
+
+
+def _lin(nhm, a, a_type, m, lda, w, out, ld_out, ws, wsb):
+    return nhm.lib.nhm_fp8_linear(a, a_type, m, lda, C.byref(w), out, ld_out, ws, wsb, None)
+
+
+def test_linear_refusals(nhm):
+    A, O, WS = 0x10000, 0x20000, 0x40000
+    need = nhm.fp8_linear_workspace_bytes(4, 64, 128, nhm.NHM_BF16)
+    assert need >= 4 * 128
+    cases = [
+        (dict(a=None), 1), (dict(out=None), 1), (dict(w=_w(nhm, w=0)), 1),
+        (dict(w=_w(nhm, k=100)), 2), (dict(w=_w(nhm, n=0)), 2), (dict(m=-1), 2), (dict(lda=64), 2),
+        (dict(ld_out=10), 2), (dict(a=A + 2), 3), (dict(w=_w(nhm, w=0x1008)), 3), (dict(out=O + 1), 3),
+        (dict(wsb=need - 1), 5), (dict(ws=None), 5), (dict(a_type=7), 4), (dict(ws=WS + 8), 3),
+    ]
+    for over, status in cases:
+        kw = dict(a=A, a_type=nhm.NHM_BF16, m=4, lda=128, w=_w(nhm), out=O, ld_out=64, ws=WS, wsb=need)
+        kw.update(over)
+        st = _lin(nhm, kw["a"], kw["a_type"], kw["m"], kw["lda"], kw["w"], kw["out"], kw["ld_out"], kw["ws"], kw["wsb"])
+        assert st == status, (over, st, nhm.lib.nhm_last_error())
+        assert nhm.lib.nhm_last_error() != b""
+
+
+def test_linear_zero_rows_is_noop(nhm):
+    assert _lin(nhm, None, nhm.NHM_BF16, 0, 128, _w(nhm), None, 64, None, 0) == 0
+
+
+def test_quant_refusals(nhm):
+    q = nhm.lib.nhm_fp8_quantize_static
+    assert q(None, 0, 8, 8, None, None, 8, None) == 0                 # empty is a no-op
+    assert q(None, 2, 8, 8, 0x100, 0x200, 8, None) == 1
+    assert q(0x100, 2, 8, 4, 0x100, 0x200, 8, None) == 2
+    assert q(0x101, 2, 8, 8, 0x100, 0x200, 8, None) == 3
+    assert q(0x100, -1, 8, 8, 0x100, 0x200, 8, None) == 2
+
+
+def _params(nhm, **over):
+    g = nhm.Geometry(**nhm.GEOMETRY)
+    lay = nhm.mixer_layout()
+    d = dict(in_proj=_w(nhm, n=lay["d_in_proj"], k=2688), out_proj=_w(nhm, n=2688, k=4096), conv_w=0x5000,
+             conv_b=0x6000, norm_w=0x7000, A_log=0x8000, D=0x9000, dt_bias=0xA000)
+    d.update(over)
+    return nhm._MixerParams(g, d["in_proj"], d["out_proj"], d["conv_w"], d["conv_b"], d["norm_w"], d["A_log"],
+                            d["D"], d["dt_bias"])
+
+
+def test_decode_refusals(nhm):
+    dec = nhm.lib.nhm_mixer_decode
+    need = nhm.decode_ws_layout(8)["total"]
+    H, SL, SP, CP, O, WS = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+
+    def call(p=None, hidden=H, batch=8, slots=SL, sp=SP, cp=CP, n_slots=64, out=O, ws=WS, wsb=need):
+        p = p or _params(nhm)
+        return dec(C.byref(p), hidden, batch, slots, sp, cp, n_slots, out, ws, wsb, None)
+
+    assert call(batch=0) == 0
+    assert call(hidden=None) == 1
+    assert call(ws=None) == 1
+    assert call(p=_params(nhm, conv_w=0)) == 1
+    assert call(p=_params(nhm, in_proj=_w(nhm, n=10304, k=4096))) == 2      # wrong orientation
+    assert call(p=_params(nhm, out_proj=_w(nhm, n=4096, k=2688))) == 2
+    assert call(batch=-1) == 2
+    assert call(n_slots=0) == 2
+    assert call(hidden=H + 8) == 3
+    assert call(p=_params(nhm, conv_w=0x5008)) == 3
+    assert call(wsb=need - 1) == 5
+    g = nhm.Geometry(**dict(nhm.GEOMETRY, rms_eps=0.0))
+    p = _params(nhm)
+    p.g = g
+    assert call(p=p) == 4
+
+
+def test_prefill_refusals(nhm):
+    pre = nhm.lib.nhm_mixer_prefill
+    need = nhm.prefill_ws_layout(512, 1)["total"]
+    H, CU, SL, HI, SP, CP, O, WS = [0x100000 * i for i in range(1, 9)]
+
+    def call(T=512, cu=CU, n=1, chunk=128, n_slots=4, ws=WS, wsb=need, hidden=H, hi=HI):
+        return pre(C.byref(_params(nhm)), hidden, T, cu, n, SL, hi, chunk, SP, CP, n_slots, O, ws, wsb, None)
+
+    assert call(T=0, n=0) == 0
+    assert call(T=5, n=0) == 2
+    assert call(chunk=64) == 4
+    assert call(n=5, n_slots=4) == 2
+    assert call(cu=None) == 1
+    assert call(hi=None) == 1
+    assert call(hidden=H + 4) == 3
+    assert call(wsb=need - 1) == 5
+    assert call(ws=WS + 16) == 3
+    with pytest.raises(nhm.NhmError):
+        nhm.prefill_ws_layout(512, 1, chunk=256)
+
+
+def test_workspace_sizes_grow(nhm):
+    a = nhm.prefill_ws_layout(512, 1)
+    b = nhm.prefill_ws_layout(15360, 4)
+    assert b["total"] > a["total"] > 0
+    assert a["q_in"] < a["zxbcdt"] < a["xbc_conv"] < a["y"] < a["norm"] < a["q_out"] < a["total"]
+    d = nhm.decode_ws_layout(8)
+    assert d["q_out"] + 8 * 4096 <= d["total"]

@@ -1,0 +1,110 @@
+"""a2 / a10 parity: the HIP W8A8 GEMV / GEMM against the oracle's dequantize-then-matmul.
+
+Bound (derived from the arithmetic): the kernel accumulates exact e4m3 products
+in f32 and rounds the scaled result once to bf16, so
+    |gpu - ref| <= 2^-8 |ref| + 2^-16 * S,   S = sum_k |a_k w_k| * s_a * ws_n,
+one bf16 ulp plus a generous f32 accumulation term. The block tolerance
+(max |d| <= 2e-2 RMS(ref)) is asserted as well.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nhm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_w8a8_linear_amd as m
+    return m
+
+
+def _check(nhm, a_bf16, w, ws, sa, via_e4m3=False, ld_pad=0):
+    from oracle import bf16_to_f64, e4m3_decode, fp8_linear, quantize_static
+    from tests.gpu_util import dev, host, rel_max
+    m, k = a_bf16.shape
+    n = w.shape[0]
+    q = quantize_static(a_bf16, sa)
+    ref = fp8_linear(q, w, ws, sa)
+    S = np.abs(e4m3_decode(q)) @ np.abs(e4m3_decode(w)).T * np.float64(sa[0]) * ws.astype(np.float64)[None, :]
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    a_in = dev(q) if via_e4m3 else dev(a_bf16)
+    a_type = nhm.NHM_E4M3 if via_e4m3 else nhm.NHM_BF16
+    out = torch.full((m, n + ld_pad), 0x7777, dtype=torch.int16, device="cuda")
+    if ld_pad == 0:
+        nhm.fp8_linear(a_in, W, out=out, a_type=a_type)
+    else:                                 # row stride n + ld_pad through the raw ABI
+        import ctypes as C
+        need = nhm.fp8_linear_workspace_bytes(m, n, k, a_type)
+        wsb = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+        st = nhm.lib.nhm_fp8_linear(C.c_void_p(a_in.data_ptr()), a_type, m, k, C.byref(W.struct),
+                                    C.c_void_p(out.data_ptr()), n + ld_pad, C.c_void_p(wsb.data_ptr()),
+                                    wsb.numel(), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, nhm.lib.nhm_last_error()
+    torch.cuda.synchronize()
+    o = host(out)
+    got = bf16_to_f64(o[:, :n])
+    if ld_pad:
+        assert np.all(o[:, n:] == 0x7777)
+    assert got.shape == ref.shape == (m, n) and got.size == m * n
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * S
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), f"at {worst}: got {got[worst]} ref {ref[worst]} bound {bound[worst]}"
+    assert rel_max(got, ref) <= 2e-2
+    return o
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 10304, 2688), (8, 10304, 2688), (512, 10304, 2688),
+                                   (1, 2688, 4096), (512, 2688, 4096), (64, 4096, 4096)])
+def test_linear_sweep_shapes(nhm, m, n, k):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k)
+    _check(nhm, a, w, ws, sa)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
+                                   (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688)])
+def test_linear_ragged(nhm, m, n, k):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=7)
+    _check(nhm, a, w, ws, sa)
+
+
+@pytest.mark.parametrize("m", [1, 8, 64])
+def test_linear_prequantized_input(nhm, m):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, 2688, 4096, extra=3)
+    _check(nhm, a, w, ws, sa, via_e4m3=True)
+
+
+@pytest.mark.parametrize("m", [2, 100])
+def test_linear_strided_output(nhm, m):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, 520, 512, extra=4)
+    _check(nhm, a, w, ws, sa, ld_pad=12)
+
+
+@pytest.mark.parametrize("m", [8, 512])
+def test_linear_deterministic(nhm, m):
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, 10304, 2688)
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    ad = dev(a)
+    o1 = host(nhm.fp8_linear(ad, W))
+    o2 = host(nhm.fp8_linear(ad, W))
+    assert np.array_equal(o1, o2)
+
+
+def test_linear_zero_rows(nhm):
+    from tests.gpu_util import dev
+    from workloads import linear_case
+    _, w, ws, sa = linear_case(1, 64, 128)
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    a = torch.empty((0, 128), dtype=torch.int16, device="cuda")
+    out = nhm.fp8_linear(a, W)
+    assert out.shape == (0, 64)

@@ -34,8 +34,9 @@ def test_decode_is_prefill_of_length_one(case):
     out_d, _ = mixer_decode(p, h[:2], np.array([2, 0]), sp1, cp1)
     sp2, cp2 = sp.copy(), cp.copy()
     out_p, _ = mixer_prefill(p, h[:2], np.array([0, 1, 2]), np.array([2, 0]), np.array([1, 1]), sp2, cp2)
-    assert np.array_equal(out_d, out_p)
-    assert np.array_equal(sp1, sp2) and np.array_equal(cp1, cp2)
+    # equal up to the float64 summation order of the batched projection
+    assert rel_max(out_d, out_p) < 1e-9
+    assert np.max(np.abs(sp1 - sp2)) <= 1e-6 * np.max(np.abs(sp2)) and np.array_equal(cp1, cp2)
     assert not np.array_equal(sp1[2], sp[2]) and np.array_equal(sp1[1], sp[1])
 
 
