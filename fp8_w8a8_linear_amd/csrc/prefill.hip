@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a) {
     for (int r = 0; r < kConvRun; ++r) {
         const int64_t tok = t0 + r;
         if (tok >= a.T) break;
-        if (tok >= a.cu_seqlens[i + 1]) {      // next non-empty sequence starts here
-            while (tok >= a.cu_seqlens[i + 1]) ++i;
+        if (i < a.n_seqs - 1 && tok >= a.cu_seqlens[i + 1]) {   // the next non-empty sequence starts here
+            while (i < a.n_seqs - 1 && tok >= a.cu_seqlens[i + 1]) ++i;
 #pragma unroll
             for (int j = 0; j < 3; ++j) unpack8(init_row(a, i, j, c8), u[j]);
         }
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
 // final state in the pool row (read first, written last by this workgroup only).
 __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
     const int i = blockIdx.x, h = blockIdx.y, pb = blockIdx.z, t = threadIdx.x;
-    const int c0 = a.seq_chunk0[i], c1 = a.seq_chunk0[i + 1];
+    const int c0 = min(a.seq_chunk0[i], a.max_chunks), c1 = min(a.seq_chunk0[i + 1], a.max_chunks);
     const int64_t off = (int64_t)pb * 8 * kDS + 4 * t;
     float4* pool = reinterpret_cast<float4*>(a.ssm_pool + ((int64_t)a.slot_idx[i] * a.n_heads + h) * kHP * kDS + off);
     float4 H = a.has_initial[i] ? *pool : make_float4(0.f, 0.f, 0.f, 0.f);
