@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Mixer throughput on one MI355X: paged decode B=8 through 23 stacked blocks (the
+headline line) and prefill of one 512-token sequence through one block.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+A step is one decode token for each of 8 sequences through all 23 mixer blocks
+(nhm_mixer_decode per block, state rows updated in place), replayed as one HIP
+graph. Inputs are seeded synthetic tensors already resident in HBM. Before timing,
+layers 0 and 1 of one step are checked against the oracle (block parity and the
+updated f32 states); that same oracle run, timed on the host cores, is the
+cpu_baseline. Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N_LAYERS, BATCH, SLOTS, HIDDEN, INNER = 23, 8, 64, 2688, 4096
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+WORKLOAD_DECODE = 2          # paged decode B=8, 23 blocks
+WORKLOAD_PREFILL = 3         # prefill 512, one block
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes_per_layer(B):
+    """Algorithmic HBM bytes of one decode call: weights + scales + small params once,
+    and per sequence the f32 state row read+write, the conv window read+write and the
+    bf16 block input and output."""
+    w = 10304 * 2688 + 2688 * 4096
+    scales = 4 * (10304 + 2688 + 2)
+    small = 6144 * 4 * 2 + 6144 * 2 + 4096 * 2 + 3 * 64 * 4
+    per_seq = 2 * 64 * 64 * 128 * 4 + 2 * 3 * 6144 * 2 + 2 * 2688 * 2 + 4
+    return w + scales + small + B * per_seq
+
+
+def gemv_bytes(m, n, k):
+    """Algorithmic bytes of one W8A8 GEMV: weight + per-channel scales + e4m3 input + bf16 output."""
+    return n * k + 4 * n + m * k + 2 * m * n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle parity sample and cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the mixer shards by sequence with no "
+              "collective, so an N-GPU figure is N independent copies of this one", file=sys.stderr)
+        sys.exit(2)
+    if args.steps <= 0:
+        print("--steps must be positive", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_w8a8_linear_amd as nhm
+    from workloads import block_params, conv_pool, hidden, slots, ssm_pool
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    # ------------------------------------------------------------ decode inputs
+    t0 = time.time()
+    params, host_params, spools, cpools, host_pools = [], [], [], [], {}
+    for layer in range(N_LAYERS):
+        p = block_params(WORKLOAD_DECODE, layer)
+        sp, cp = ssm_pool(WORKLOAD_DECODE, layer, SLOTS), conv_pool(WORKLOAD_DECODE, layer, SLOTS)
+        if layer < 2:
+            host_params.append(p)
+            host_pools[layer] = (sp, cp)
+        params.append(nhm.MixerParams(nhm.Fp8Weight(up(p["in_w"]), up(p["in_w_scale"]), up(p["in_a_scale"])),
+                                      nhm.Fp8Weight(up(p["out_w"]), up(p["out_w_scale"]), up(p["out_a_scale"])),
+                                      up(p["conv_w"]), up(p["conv_b"]), up(p["norm_w"]), up(p["A_log"]),
+                                      up(p["D"]), up(p["dt_bias"])))
+        spools.append(up(sp))
+        cpools.append(up(cp))
+        if layer % 6 == 5:
+            log(f"generated {layer + 1}/{N_LAYERS} blocks ({time.time() - t0:.0f} s)")
+    sl_host = slots(WORKLOAD_DECODE, BATCH, SLOTS)
+    x_host = hidden(WORKLOAD_DECODE, BATCH)
+    sl = up(sl_host)
+    x0 = up(x_host)
+    lay = nhm.decode_ws_layout(BATCH)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=dev)
+    acts = [x0] + [torch.empty((BATCH, HIDDEN), dtype=torch.int16, device=dev) for _ in range(N_LAYERS)]
+    torch.cuda.synchronize()
+    log(f"decode inputs resident ({time.time() - t0:.0f} s)")
+
+    def step(stream=None):
+        for l in range(N_LAYERS):
+            nhm.mixer_decode(params[l], acts[l], sl, spools[l], cpools[l], acts[l + 1], ws, stream=stream)
+
+    # ------------------------------------------------------------ parity sample + cpu baseline
+    parity, cpu = None, None
+    if not args.no_cpu:
+        from oracle import mixer_decode as oracle_decode
+        from oracle.parity import block_parity, rel_l2
+        import threadpoolctl
+        parity = {}
+        t_layers = []
+        x_in = x_host
+        for layer in range(2):
+            nhm.mixer_decode(params[layer], acts[layer], sl, spools[layer], cpools[layer], acts[layer + 1], ws)
+            torch.cuda.synchronize()
+            out = acts[layer + 1].cpu().numpy().view(np.uint16)
+            wsn = ws.cpu().numpy()
+            q = wsn[lay["q_out"]:lay["q_out"] + BATCH * INNER].reshape(BATCH, INNER)
+            nrm = wsn[lay["norm"]:lay["norm"] + BATCH * INNER * 2].view(np.uint16).reshape(BATCH, INNER)
+            st_gpu = spools[layer].cpu().numpy()
+            sp, cp = host_pools[layer]
+            spr, cpr = sp.copy(), cp.copy()
+            tc = time.perf_counter()
+            ref, res = oracle_decode(host_params[layer], x_in, sl_host, spr, cpr)
+            t_layers.append(time.perf_counter() - tc)
+            st_err = max(rel_l2(st_gpu[s], spr[s]) for s in sl_host)
+            assert st_err <= 1e-3, f"layer {layer}: state rel l2 {st_err}"
+            entry = {"state_rel_l2_max": float(f"{st_err:.3e}")}
+            entry.update(block_parity(out, q, nrm, ref, res["norm"], res["q_out"], host_params[layer]))
+            parity[f"layer{layer}"] = entry
+            x_in = out
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        t_layer = float(np.mean(t_layers))
+        cpu = {"value": round(BATCH / (N_LAYERS * t_layer), 4), "unit": "tokens/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"oracle decode of layers 0-1 of one B={BATCH} step ({t_layer:.2f} s/layer), scaled to 23 layers"}
+        log(f"parity sample ok: {parity}; oracle {t_layer:.2f} s/layer on {cores} threads")
+
+    # ------------------------------------------------------------ graph capture and timing
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    if not ms_step > 0:
+        print("refusing to report a rate over a non-positive window", file=sys.stderr)
+        sys.exit(3)
+    tok_s = BATCH / (ms_step * 1e-3)
+    step_bytes = N_LAYERS * decode_bytes_per_layer(BATCH)
+    log(f"decode step {ms_step * 1e3:.1f} us, {tok_s:.0f} tokens/s, step HBM {step_bytes / ms_step / 1e6:.0f} GB/s")
+
+    # ------------------------------------------------------------ dominant kernel: in_proj GEMV, m=8
+    s = torch.cuda.current_stream()
+    qin = ws[lay["q_in"]:lay["q_in"] + BATCH * HIDDEN].view(BATCH, HIDDEN)
+    gout = torch.empty((BATCH, 10304), dtype=torch.int16, device=dev)
+    gws = torch.zeros(max(nhm.fp8_linear_workspace_bytes(BATCH, 10304, HIDDEN, nhm.NHM_E4M3), 256),
+                      dtype=torch.uint8, device=dev)
+    reps = 23 * 20
+    for l in range(N_LAYERS):
+        nhm.fp8_linear(qin, params[l].in_proj, out=gout, ws=gws, a_type=nhm.NHM_E4M3)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(s)
+    for r in range(reps):
+        nhm.fp8_linear(qin, params[r % N_LAYERS].in_proj, out=gout, ws=gws, a_type=nhm.NHM_E4M3)
+    g1.record(s)
+    torch.cuda.synchronize()
+    gemv_us = g0.elapsed_time(g1) * 1e3 / reps
+    gb = gemv_bytes(BATCH, 10304, HIDDEN)
+    achieved = gb / (gemv_us * 1e-6) / 1e9
+    log(f"in_proj GEMV m=8: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s")
+
+    # ------------------------------------------------------------ prefill 512, one block
+    pp = block_params(WORKLOAD_PREFILL, 0)
+    ppar = nhm.MixerParams(nhm.Fp8Weight(up(pp["in_w"]), up(pp["in_w_scale"]), up(pp["in_a_scale"])),
+                           nhm.Fp8Weight(up(pp["out_w"]), up(pp["out_w_scale"]), up(pp["out_a_scale"])),
+                           up(pp["conv_w"]), up(pp["conv_b"]), up(pp["norm_w"]), up(pp["A_log"]), up(pp["D"]),
+                           up(pp["dt_bias"]))
+    T = 512
+    ph = up(hidden(WORKLOAD_PREFILL, T))
+    psp, pcp = up(ssm_pool(WORKLOAD_PREFILL, 0, 2)), up(conv_pool(WORKLOAD_PREFILL, 0, 2))
+    pcu, psl, phi = up(np.array([0, T], np.int32)), up(np.array([1], np.int32)), up(np.array([1], np.int32))
+    pws = torch.zeros(nhm.prefill_ws_layout(T, 1)["total"], dtype=torch.uint8, device=dev)
+    pout = torch.empty((T, HIDDEN), dtype=torch.int16, device=dev)
+
+    def pstep():
+        nhm.mixer_prefill(ppar, ph, pcu, psl, phi, psp, pcp, pout, pws)
+
+    pg = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        pstep()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(pg, stream=cap):
+        pstep()
+    for _ in range(5):
+        pg.replay()
+    torch.cuda.synchronize()
+    preps = 50
+    e0.record()
+    for _ in range(preps):
+        pg.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    pre_us = e0.elapsed_time(e1) * 1e3 / preps
+    # the two fp8 GEMMs of that block, alone
+    gemm = {}
+    for name, (n, k) in {"in_proj": (10304, 2688), "out_proj": (2688, 4096)}.items():
+        a = torch.randint(0, 0x7e, (T, k), dtype=torch.uint8, device=dev)
+        w = ppar.in_proj if name == "in_proj" else ppar.out_proj
+        o = torch.empty((T, n), dtype=torch.int16, device=dev)
+        for _ in range(3):
+            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
+        torch.cuda.synchronize()
+        g0.record(s)
+        for _ in range(50):
+            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
+        g1.record(s)
+        torch.cuda.synchronize()
+        us = g0.elapsed_time(g1) * 1e3 / 50
+        gemm[name] = {"us": round(us, 2), "tflops": round(2 * T * n * k / (us * 1e-6) / 1e12, 1)}
+    gemm_us = gemm["in_proj"]["us"] + gemm["out_proj"]["us"]
+    gemm_tflops = 2 * T * 38707200 / (gemm_us * 1e-6) / 1e12
+    log(f"prefill 512: {pre_us:.1f} us/block, {T / (pre_us * 1e-6):.0f} tokens/s; GEMMs {gemm}")
+
+    line = {
+        "metric": "Mamba2-mixer tokens/s (decode b=8, prefill 512) + % HBM / fp8-MFMA peak",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3xe4m3->f32 GEMMs, f32 SSM state, bf16 activations",
+        "data": "synthetic (seeded; no checkpoint)",
+        "config": {"workload": "paged decode, 8 sequences x 1 token through 23 stacked NemotronH Mamba2 mixer "
+                               "blocks (hidden 2688, 64 heads x 64, d_state 128, 8 groups), pool of 64 slots",
+                   "global_batch": BATCH, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "decode_step_hbm": {"bytes": step_bytes, "achieved_GBs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                            "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (in_proj 10304x2688, m=8)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(gemv_us, 3), "bytes_per_launch": gb},
+        "prefill_512": {"tokens_per_s": round(T / (pre_us * 1e-6), 1), "us_per_block": round(pre_us, 1),
+                        "gemm": gemm, "gemm_bound": "mfma", "gemm_tflops": round(gemm_tflops, 1),
+                        "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
+        "parity_sample": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -194,7 +194,7 @@ def prefill_ws_layout(n_tokens, n_seqs, chunk=128, g=GEOMETRY):
 
 
 def mixer_decode(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out, ws, stream=None):
-    """One decode token per sequence; pools updated in place. ws: zero-filled uint8 device tensor."""
+    """One decode token per sequence; pools updated in place. ws: uint8 device tensor of the layout size."""
     batch = int(hidden.shape[0])
     _check(lib.nhm_mixer_decode(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
                                 _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws), ws.numel(),
@@ -204,7 +204,7 @@ def mixer_decode(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out
 
 def mixer_prefill(params: MixerParams, hidden, cu_seqlens, slot_idx, has_initial, ssm_pool, conv_pool, out, ws,
                   chunk=128, stream=None):
-    """Varlen prefill of packed sequences; pools updated in place. ws: zero-filled uint8 device tensor."""
+    """Varlen prefill of packed sequences; pools updated in place. ws: uint8 device tensor of the layout size."""
     n_tokens = int(hidden.shape[0])
     n_seqs = int(slot_idx.shape[0])
     _check(lib.nhm_mixer_prefill(C.byref(params.struct), _ptr(hidden), n_tokens, _ptr(cu_seqlens), n_seqs,

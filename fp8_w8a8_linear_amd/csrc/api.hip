@@ -36,7 +36,8 @@ static nhm_status check_geometry(const nhm_geometry* g) {
                     g->head_dim, g->d_state, g->conv_width);
     if (g->n_heads % g->n_groups != 0)
         return fail(NHM_ERR_UNSUPPORTED, "n_heads %d is not a multiple of n_groups %d", g->n_heads, g->n_groups);
-    if (g->hidden % 16 != 0) return fail(NHM_ERR_UNSUPPORTED, "hidden %d is not a multiple of 16", g->hidden);
+    if (g->hidden % 16 != 0 || g->hidden > 16384)
+        return fail(NHM_ERR_UNSUPPORTED, "hidden %d must be a multiple of 16 and at most 16384", g->hidden);
     if (!(g->rms_eps > 0.f) || !isfinite(g->rms_eps))
         return fail(NHM_ERR_UNSUPPORTED, "rms_eps must be finite and > 0 (got %g)", (double)g->rms_eps);
     return NHM_OK;
@@ -76,23 +77,14 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
 
 // ---------------------------------------------------------------- workspace layouts
 
-struct LinearWs {
-    size_t q, gemv, total;
-};
-static LinearWs linear_ws(int64_t m, int64_t n, int64_t k, nhm_dtype t) {
-    LinearWs l{};
-    size_t off = 0;
-    l.q = off;
-    if (t == NHM_BF16) off += align_up((size_t)m * (size_t)k, 256);
-    l.gemv = off;
-    if (m <= 16) off += gemv_workspace_bytes(m, n, k);
-    l.total = off;
-    return l;
+// bytes of the e4m3 copy of a bf16 activation (the only workspace nhm_fp8_linear needs)
+static size_t linear_ws(int64_t m, int64_t k, nhm_dtype t) {
+    return t == NHM_BF16 ? align_up((size_t)m * (size_t)k, 256) : 0;
 }
 
 struct MixerWs {
     nhm_ws_layout pub;
-    size_t gemv_in, gemv_out, group_cnt, chunk_info, seq_chunk0, chunk_cs, chunk_dt, chunk_state;
+    size_t chunk_info, seq_chunk0, chunk_cs, chunk_dt, chunk_state;
     int max_chunks;
 };
 
@@ -101,12 +93,8 @@ static MixerWs decode_ws(const nhm_geometry* g, int32_t batch) {
     fill_layout(g, &l);
     MixerWs w{};
     const size_t B = (size_t)batch;
-    const int64_t mg = batch < 16 ? batch : 16;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
-    w.gemv_in = take(gemv_workspace_bytes(mg, l.d_in_proj, g->hidden));
-    w.gemv_out = take(gemv_workspace_bytes(mg, g->hidden, l.d_inner));
-    w.group_cnt = take(B * g->n_groups * sizeof(unsigned));
     w.pub.q_in = take(B * g->hidden);
     w.pub.zxbcdt = take(B * l.d_in_proj * 2);
     w.pub.xbc_conv = take(B * l.conv_dim * 2);
@@ -122,13 +110,10 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     fill_layout(g, &l);
     MixerWs w{};
     const size_t Ts = (size_t)T;
-    const int64_t mg = T < 16 ? T : 16;
     w.max_chunks = (int)(T / chunk + n);
     const size_t C = (size_t)w.max_chunks;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
-    w.gemv_in = take(gemv_workspace_bytes(mg, l.d_in_proj, g->hidden));
-    w.gemv_out = take(gemv_workspace_bytes(mg, g->hidden, l.d_inner));
     w.pub.q_in = take(Ts * g->hidden);
     w.pub.zxbcdt = take(Ts * l.d_in_proj * 2);
     w.pub.xbc_conv = take(Ts * l.conv_dim * 2);
@@ -144,11 +129,15 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     return w;
 }
 
-// One projection of the block on an e4m3 activation: GEMV for m <= 16, else GEMM.
-static nhm_status project(const uint8_t* a, int64_t m, const nhm_fp8_weight& w, uint16_t* out, int64_t ld_out,
-                          const ConvEpilogue* conv, void* gemv_ws, hipStream_t st) {
-    if (m <= 16) return launch_gemv(a, w.k, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, gemv_ws, st);
-    return launch_gemm(a, w.k, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
+// The weight-streaming GEMV serves m <= 16 (and k up to 16384); the tiled GEMM the rest.
+static bool use_gemv(int64_t m, int64_t k) { return m <= 16 && k <= 16384; }
+
+// One projection on an e4m3 activation [m, lda].
+static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
+                          int64_t ld_out, const ConvEpilogue* conv, hipStream_t st) {
+    if (use_gemv(m, w.k))
+        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st);
+    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
 }
 
 static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
@@ -214,7 +203,7 @@ nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t cols
 
 size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type) {
     if (m <= 0 || n <= 0 || k <= 0) return 0;
-    return linear_ws(m, n, k, a_type).total;
+    return linear_ws(m, k, a_type);
 }
 
 nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
@@ -236,25 +225,22 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
     if (!aligned(a, 16) || (a_type == NHM_BF16 ? ld_a % 8 : ld_a % 16) != 0)
         return fail(NHM_ERR_ALIGN, "a must be 16-byte aligned with 16-byte row stride");
     if (!aligned(out, 2)) return fail(NHM_ERR_ALIGN, "out must be 2-byte aligned");
-    const LinearWs l = linear_ws(m, w->n, w->k, a_type);
-    if (l.total > 0 && (!ws || ws_bytes < l.total))
-        return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", l.total, ws ? ws_bytes : (size_t)0);
+    const size_t need = linear_ws(m, w->k, a_type);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (ws && !aligned(ws, 256)) return fail(NHM_ERR_ALIGN, "ws must be 256-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* aq = static_cast<const uint8_t*>(a);
     int64_t lda = ld_a;
     char* wsb = static_cast<char*>(ws);
     if (a_type == NHM_BF16) {
-        uint8_t* q = reinterpret_cast<uint8_t*>(wsb + l.q);
+        uint8_t* q = reinterpret_cast<uint8_t*>(wsb);
         launch_quantize(static_cast<const uint16_t*>(a), m, w->k, ld_a, w->a_scale, q, w->k, st);
         if ((s = check_launch("quantize_static")) != NHM_OK) return s;
         aq = q;
         lda = w->k;
     }
-    if (m <= 16)
-        return launch_gemv(aq, lda, (int)m, w->w, w->w_scale, w->a_scale, w->n, w->k, out, ld_out, nullptr,
-                           wsb + l.gemv, st);
-    return launch_gemm(aq, lda, m, w->w, w->w_scale, w->a_scale, w->n, w->k, out, ld_out, st);
+    return project(aq, lda, m, *w, out, ld_out, nullptr, st);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
@@ -312,8 +298,7 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
         ConvEpilogue ce{slot_idx + r0, conv_pool, p->conv_w, p->conv_b, xc + (int64_t)r0 * l.conv_dim, l.xbc_off,
                         l.conv_dim};
-        s = project(q_in + (int64_t)r0 * H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce,
-                    wsb + w.gemv_in, st);
+        s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce, st);
         if (s != NHM_OK) return s;
     }
     DecodeSsmArgs da;
@@ -324,27 +309,22 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
     da.A_log = p->A_log;
     da.D = p->D;
     da.dt_bias = p->dt_bias;
-    da.norm_w = p->norm_w;
-    da.out_a_scale = p->out_proj.a_scale;
     da.y = reinterpret_cast<uint16_t*>(wsb + w.pub.y);
-    da.norm = reinterpret_cast<uint16_t*>(wsb + w.pub.norm);
-    da.q_out = q_out;
-    da.group_counters = reinterpret_cast<unsigned*>(wsb + w.group_cnt);
     da.n_heads = p->g.n_heads;
     da.n_groups = p->g.n_groups;
     da.d_in_proj = l.d_in_proj;
     da.conv_dim = l.conv_dim;
     da.d_inner = l.d_inner;
-    da.z_off = l.z_off;
     da.dt_off = l.dt_off;
     da.b_off = l.b_off;
     da.c_off = l.c_off;
-    da.eps = p->g.rms_eps;
     if ((s = launch_decode_ssm(da, batch, st)) != NHM_OK) return s;
+    GnormArgs ga{batch, p->g.n_groups, l.d_inner, l.d_in_proj, l.z_off, p->g.rms_eps, da.y, zx, p->norm_w,
+                 p->out_proj.a_scale, reinterpret_cast<uint16_t*>(wsb + w.pub.norm), q_out};
+    if ((s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        s = project(q_out + (int64_t)r0 * l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, nullptr,
-                    wsb + w.gemv_out, st);
+        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, nullptr, st);
         if (s != NHM_OK) return s;
     }
     return NHM_OK;
@@ -384,7 +364,7 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     if (n_tokens > 0) {
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
-        if ((s = project(q_in, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, wsb + w.gemv_in, st)) != NHM_OK) return s;
+        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, st)) != NHM_OK) return s;
     }
     PrefillArgs a;
     a.T = n_tokens;
@@ -426,7 +406,7 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     a.q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
     if ((s = launch_prefill_mid(a, st)) != NHM_OK) return s;
     if (n_tokens > 0)
-        return project(a.q_out, n_tokens, p->out_proj, out, H, nullptr, wsb + w.gemv_out, st);
+        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, nullptr, st);
     return NHM_OK;
 }
 

@@ -1,14 +1,10 @@
 // Decode-step recurrence: one workgroup per (sequence, head) advances that head's
 // f32 state rows [head_dim=64][d_state=128] of pool row slot_idx[b] in place,
 //     h <- dA * h + (dt * x) (x) B,     y = h . C + D * x,
-// and stores y as bf16. HBM-bound: the state is read and written once (64 KB per
-// workgroup), streamed as float4 with every wave covering whole 512-byte rows.
-//
-// The gated group RMSNorm and the out_proj activation quant are fused behind it:
-// the last of the heads_per_group workgroups of a (sequence, group) to finish
-// (atomic counter, reset by that workgroup) normalizes the group's 512 channels
-// ([PR1288] "What it does": Mamba2ChunkScan -> RmsNormGatedGroup(n_groups) ->
-// out_proj (FP8 W8A8)) and writes their e4m3 codes for the out_proj GEMV.
+// and stores y as bf16 ([PR1288] "What it does": the paged arm advances the
+// gathered recurrent rows in place). HBM-bound: the state is read and written once
+// (64 KB per workgroup), streamed as 16-byte vectors with every half-wave covering
+// one whole 512-byte state row.
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -23,90 +19,55 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
     const int g = h / hpg;
     const int slot = a.slot_idx[b];
     __shared__ float sx[kP], sB[kN], sC[kN];
-    __shared__ float s_red[4];
-    __shared__ int s_last;
 
     uint16_t* yrow = a.y + (int64_t)b * a.d_inner + h * kP;
-    if (slot >= 0) {
-        const uint16_t* xr = a.xbc_conv + (int64_t)b * a.conv_dim;
-        if (t < kP) sx[t] = bf16_to_f32(xr[h * kP + t]);
-        if (t < kN) sB[t] = bf16_to_f32(xr[a.b_off + g * kN + t]);
-        else sC[t - kN] = bf16_to_f32(xr[a.c_off + g * kN + t - kN]);
-        const float dt = softplus(bf16_to_f32(a.zxbcdt[(int64_t)b * a.d_in_proj + a.dt_off + h]) + a.dt_bias[h]);
-        const float dA = __expf(dt * -__expf(a.A_log[h]));
-        __syncthreads();
-
-        // element e = 4 * (t + 256 i): p = t / 32 + 8 i, n = 4 * (t % 32) .. + 3
-        v4f* st = reinterpret_cast<v4f*>(a.ssm_pool + (((int64_t)slot * a.n_heads + h) * kP) * kN);
-        const int n0 = 4 * (t & 31);
-        v4f hv[8];
+    if (slot < 0) {                      // padded row: zero output, no state touched
+        if (t < kP) yrow[t] = 0;
+        return;
+    }
+    // element e = 4 * (t + 256 i): p = t / 32 + 8 i, n = 4 * (t % 32) .. + 3
+    v4f* st = reinterpret_cast<v4f*>(a.ssm_pool + (((int64_t)slot * a.n_heads + h) * kP) * kN);
+    v4f hv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = __builtin_nontemporal_load(st + t + 256 * i);
-        const float b0 = sB[n0], b1 = sB[n0 + 1], b2 = sB[n0 + 2], b3 = sB[n0 + 3];
-        const float c0 = sC[n0], c1 = sC[n0 + 1], c2 = sC[n0 + 2], c3 = sC[n0 + 3];
-        float yp[8];
+    for (int i = 0; i < 8; ++i) hv[i] = __builtin_nontemporal_load(st + t + 256 * i);
+
+    const uint16_t* xr = a.xbc_conv + (int64_t)b * a.conv_dim;
+    if (t < kP) sx[t] = bf16_to_f32(xr[h * kP + t]);
+    if (t < kN) sB[t] = bf16_to_f32(xr[a.b_off + g * kN + t]);
+    else sC[t - kN] = bf16_to_f32(xr[a.c_off + g * kN + t - kN]);
+    const float dt = softplus(bf16_to_f32(a.zxbcdt[(int64_t)b * a.d_in_proj + a.dt_off + h]) + a.dt_bias[h]);
+    const float dA = __expf(dt * -__expf(a.A_log[h]));
+    __syncthreads();
+
+    const int n0 = 4 * (t & 31);
+    const float b0 = sB[n0], b1 = sB[n0 + 1], b2 = sB[n0 + 2], b3 = sB[n0 + 3];
+    const float c0 = sC[n0], c1 = sC[n0 + 1], c2 = sC[n0 + 2], c3 = sC[n0 + 3];
+    float yp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = (t >> 5) + 8 * i;
+        const float u = dt * sx[p];
+        v4f v = hv[i];
+        v[0] = fmaf(dA, v[0], u * b0);
+        v[1] = fmaf(dA, v[1], u * b1);
+        v[2] = fmaf(dA, v[2], u * b2);
+        v[3] = fmaf(dA, v[3], u * b3);
+        __builtin_nontemporal_store(v, st + t + 256 * i);
+        yp[i] = v[0] * c0 + v[1] * c1 + v[2] * c2 + v[3] * c3;
+    }
+    // reduce over the 32 lanes that share p
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) yp[i] += __shfl_xor(yp[i], o, kWave);
+    }
+    if ((t & 31) == 0) {
+        const float Dh = a.D[h];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int p = (t >> 5) + 8 * i;
-            const float u = dt * sx[p];
-            v4f v = hv[i];
-            v[0] = fmaf(dA, v[0], u * b0);
-            v[1] = fmaf(dA, v[1], u * b1);
-            v[2] = fmaf(dA, v[2], u * b2);
-            v[3] = fmaf(dA, v[3], u * b3);
-            __builtin_nontemporal_store(v, st + t + 256 * i);
-            yp[i] = v[0] * c0 + v[1] * c1 + v[2] * c2 + v[3] * c3;
+            yrow[p] = (uint16_t)f32_to_bf16(yp[i] + Dh * sx[p]);
         }
-        // reduce over the 32 lanes that share p
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) yp[i] += __shfl_xor(yp[i], o, kWave);
-        }
-        if ((t & 31) == 0) {
-            const float Dh = a.D[h];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int p = (t >> 5) + 8 * i;
-                yrow[p] = (uint16_t)f32_to_bf16(yp[i] + Dh * sx[p]);
-            }
-        }
-    } else if (t < kP) {
-        yrow[t] = 0;   // padded row
-    }
-
-    // ---- the last head of the group runs the gated RMSNorm + e4m3 quant of the group
-    __threadfence();
-    __syncthreads();
-    if (t == 0) {
-        unsigned* cnt = a.group_counters + b * a.n_groups + g;
-        s_last = atomicAdd(cnt, 1u) == (unsigned)(hpg - 1);
-        if (s_last) *cnt = 0u;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    const int gw = a.d_inner / a.n_groups;                  // channels per group (512)
-    const int64_t c0 = (int64_t)g * gw;
-    const uint16_t* yr = a.y + (int64_t)b * a.d_inner + c0;
-    const uint16_t* zr = a.zxbcdt + (int64_t)b * a.d_in_proj + a.z_off + c0;
-    float ss = 0.f;
-    for (int c = t; c < gw; c += 256) {
-        const float v = bf16_to_f32(yr[c]) * silu(bf16_to_f32(zr[c]));
-        ss += v * v;
-    }
-    ss = wave_sum(ss);
-    if ((t & 63) == 0) s_red[t >> 6] = ss;
-    __syncthreads();
-    const float tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    const float r = 1.0f / sqrtf(tot / (float)gw + a.eps);
-    const float so = *a.out_a_scale;
-    for (int c = t; c < gw; c += 256) {
-        const float v = bf16_to_f32(yr[c]) * silu(bf16_to_f32(zr[c]));
-        const uint32_t ob = f32_to_bf16(v * r * bf16_to_f32(a.norm_w[c0 + c]));
-        a.norm[(int64_t)b * a.d_inner + c0 + c] = (uint16_t)ob;
-        a.q_out[(int64_t)b * a.d_inner + c0 + c] = (uint8_t)quant_bf16(ob, so);
     }
 }
 

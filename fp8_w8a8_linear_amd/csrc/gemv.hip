@@ -2,45 +2,21 @@
 //
 // The problem is HBM-bound: every weight byte is read exactly once and the
 // activations (m x k e4m3, a few KB) stay in L2/L1. The contraction still runs on
-// the 16x16x128 e4m3 MFMA: the 16 weight rows of a wave are the A operand, the
-// (zero-padded) 16 activation rows the B operand, so the VALU never converts fp8.
+// the 16x16x128 e4m3 MFMA: 16 weight rows are the A operand, the (zero-padded) 16
+// activation rows the B operand, so the VALU never converts fp8.
 //
-// Decomposition: a workgroup of 4 waves owns 64 output features (16 per wave) and
-// one slice of the k-steps (128 k each). All weight loads of the slice are issued
-// before the first MFMA so each wave keeps its whole slice in flight. When k is
-// split across workgroups, each workgroup stores an f32 partial and the last one
-// to arrive (atomic counter) sums the partials in split order -- deterministic,
-// no float atomics -- and runs the epilogue. The counter is reset to 0 by that
-// last workgroup.
+// Decomposition: one workgroup owns 16 output features and the whole k range; its
+// waves take the 128-wide k-steps round-robin (neighbouring waves read neighbouring
+// 128-byte pieces of each row) and issue all their weight loads before the first
+// MFMA, so a wave keeps its whole share in flight. The per-wave partial tiles are
+// summed through LDS in wave order -- deterministic, and no communication between
+// workgroups (an agent-scope fence would write back the L2 of every XCD).
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
 namespace nhm {
 
-constexpr int kGemvRows = 64;          // output features per workgroup
-constexpr int kGemvMaxSteps = 8;       // k-steps per workgroup (registers)
-
-GemvPlan gemv_plan(int64_t n, int64_t k) {
-    GemvPlan p;
-    p.row_blocks = (int)((n + kGemvRows - 1) / kGemvRows);
-    p.ksteps = (int)((k + 127) / 128);
-    // about 640 workgroups (2.5 per CU), at least 4 and at most 8 k-steps each
-    long target = ((long)p.ksteps * p.row_blocks + 639) / 640;
-    int sps = (int)(target < 4 ? 4 : target);
-    if (sps > kGemvMaxSteps) sps = kGemvMaxSteps;
-    if (sps > p.ksteps) sps = p.ksteps;
-    if (sps < 1) sps = 1;
-    p.ksplit = (p.ksteps + sps - 1) / sps;
-    p.steps_per_split = (p.ksteps + p.ksplit - 1) / p.ksplit;
-    return p;
-}
-
-size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-    const GemvPlan p = gemv_plan(n, k);
-    size_t bytes = align_up((size_t)p.row_blocks * sizeof(unsigned), 256);
-    if (p.ksplit > 1) bytes += align_up((size_t)p.ksplit * (size_t)n * (size_t)m * sizeof(float), 256);
-    return bytes;
-}
+constexpr int kGemvMaxSteps = 8;       // k-steps per wave held in registers
 
 // 32 bytes of row `row` starting at byte `kb`, zero beyond k or for rows >= nrows.
 // Weight rows are streamed once: non-temporal loads keep them out of the caches.
@@ -68,73 +44,50 @@ struct GemvArgs {
     const uint8_t* a; int64_t lda; int m;
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
     uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: 8-byte aligned rows
-    float* partial; unsigned* counters;
-    int ksplit, steps_per_split, ksteps;
+    int ksteps;
     ConvEpilogue conv;
 };
 
-template <bool kConv>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs g) {
+template <int kWaves, bool kConv>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
+    __shared__ v4f s_red[kWaves][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rb = blockIdx.x, split = blockIdx.y;
-    const int64_t row = (int64_t)rb * kGemvRows + wave * 16 + (lane & 15);   // A operand row
-    const int col = lane & 15;                                                // B operand column (token)
-    const int s0 = split * g.steps_per_split;
-    int ns = g.ksteps - s0;
-    if (ns > g.steps_per_split) ns = g.steps_per_split;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t row = n0 + (lane & 15);       // A operand row (feature)
+    const int col = lane & 15;                  // B operand column (token)
     const int64_t kq = (lane >> 4) * 32;
 
     v8i wa[kGemvMaxSteps], xb[kGemvMaxSteps];
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSteps; ++i)
-        if (i < ns) wa[i] = load32<true>(g.w, g.k, row, g.n, (int64_t)(s0 + i) * 128 + kq, g.k);
+    for (int i = 0; i < kGemvMaxSteps; ++i) {
+        const int s = wave + i * kWaves;
+        if (s < g.ksteps) wa[i] = load32<true>(g.w, g.k, row, g.n, (int64_t)s * 128 + kq, g.k);
+    }
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSteps; ++i)
-        if (i < ns) xb[i] = load32<false>(g.a, g.lda, col, g.m, (int64_t)(s0 + i) * 128 + kq, g.k);
+    for (int i = 0; i < kGemvMaxSteps; ++i) {
+        const int s = wave + i * kWaves;
+        if (s < g.ksteps) xb[i] = load32<false>(g.a, g.lda, col, g.m, (int64_t)s * 128 + kq, g.k);
+    }
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i)
-        if (i < ns) acc = mfma_e4m3(wa[i], xb[i], acc);
+        if (wave + i * kWaves < g.ksteps) acc = mfma_e4m3(wa[i], xb[i], acc);
 
-    // acc[r] = D[feature rbase + r][token col]
-    const int64_t nbase = (int64_t)rb * kGemvRows + wave * 16 + 4 * (lane >> 4);
-    if (g.ksplit > 1) {
-        __shared__ int s_last;
-        if (col < g.m) {
+    if (wave > 0) s_red[wave][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nbase + r < g.n) g.partial[((int64_t)split * g.n + nbase + r) * g.m + col] = acc[r];
-        }
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) s_last = atomicAdd(&g.counters[rb], 1u) == (unsigned)(g.ksplit - 1);
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        v4f tot = {0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < g.ksplit; ++sp) {
-            if (sp == split) {
-                tot += acc;
-            } else if (col < g.m) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (nbase + r < g.n)
-                        tot[r] += (g.partial[((int64_t)sp * g.n + nbase + r) * g.m + col]);
-            }
-        }
-        acc = tot;
-        if (threadIdx.x == 0) g.counters[rb] = 0u;
-    }
+    for (int w = 1; w < kWaves; ++w) acc += s_red[w][lane];
+
+    // acc[r] = D[feature nbase + r][token col]
     if (col >= g.m) return;
-
+    const int64_t nbase = n0 + 4 * (lane >> 4);
     const float sa = *g.a_scale;
     uint32_t hb[4];
-    float val[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t nn = nbase + r;
-        val[r] = nn < g.n ? acc[r] * sa * g.w_scale[nn] : 0.f;
-        hb[r] = f32_to_bf16(val[r]);
+        hb[r] = f32_to_bf16(nn < g.n ? acc[r] * sa * g.w_scale[nn] : 0.f);
     }
     uint16_t* o = g.out + (int64_t)col * g.ld_out + nbase;
     if (g.vec_out && nbase + 3 < g.n) {
@@ -187,23 +140,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs g) {
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, void* ws, hipStream_t st) {
-    const GemvPlan p = gemv_plan(n, k);
+                       const ConvEpilogue* conv, hipStream_t st) {
     GemvArgs g;
     g.a = a; g.lda = lda; g.m = m;
     g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
     g.out = out; g.ld_out = ld_out;
     g.vec_out = ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
-    g.counters = reinterpret_cast<unsigned*>(ws);
-    g.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                         align_up((size_t)p.row_blocks * sizeof(unsigned), 256));
-    g.ksplit = p.ksplit; g.steps_per_split = p.steps_per_split; g.ksteps = p.ksteps;
-    if (conv) g.conv = *conv; else g.conv = ConvEpilogue{};
-    const dim3 grid(p.row_blocks, p.ksplit);
-    if (conv)
-        gemv_kernel<true><<<grid, dim3(256), 0, st>>>(g);
-    else
-        gemv_kernel<false><<<grid, dim3(256), 0, st>>>(g);
+    g.ksteps = (int)((k + 127) / 128);
+    g.conv = conv ? *conv : ConvEpilogue{};
+    if (g.ksteps > 16 * kGemvMaxSteps)
+        return fail(NHM_ERR_UNSUPPORTED, "gemv: k %lld exceeds %d", (long long)k, 16 * 128 * kGemvMaxSteps);
+    // 4 waves up to 23 k-steps (k < 2944), then 8, then 16
+    const int waves = g.ksteps < 24 ? 4 : (g.ksteps <= 8 * kGemvMaxSteps ? 8 : 16);
+    const dim3 grid((unsigned)((n + 15) / 16));
+#define NHM_GEMV_LAUNCH(W)                                                  \
+    do {                                                                    \
+        if (conv) gemv_kernel<W, true><<<grid, dim3(W * 64), 0, st>>>(g);  \
+        else gemv_kernel<W, false><<<grid, dim3(W * 64), 0, st>>>(g);      \
+    } while (0)
+    if (waves == 4) NHM_GEMV_LAUNCH(4);
+    else if (waves == 8) NHM_GEMV_LAUNCH(8);
+    else NHM_GEMV_LAUNCH(16);
+#undef NHM_GEMV_LAUNCH
     return check_launch("gemv");
 }
 

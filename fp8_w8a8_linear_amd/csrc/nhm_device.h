@@ -56,6 +56,16 @@ __device__ __forceinline__ uint32_t quant_bf16(uint32_t xb, float s) {
     return e4m3_code(__fdiv_rn(bf16_to_f32(xb), s));
 }
 
+// The eight bf16 values of a 16-byte load, in memory order.
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = bf16_to_f32(w[j] & 0xffffu);
+        f[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(__expf(u)); }

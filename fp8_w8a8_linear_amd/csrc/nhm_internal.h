@@ -22,14 +22,6 @@ void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x
                      uint8_t* q, int64_t ld_q, hipStream_t st);
 
 // ---- weight-streaming GEMV for m <= 16 (gemv.hip)
-struct GemvPlan {
-    int row_blocks;     // ceil(n / 64)
-    int ksteps;         // ceil(k / 128)
-    int steps_per_split;
-    int ksplit;
-};
-GemvPlan gemv_plan(int64_t n, int64_t k);
-size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k);   // partials + counters
 
 // Epilogue of the in_proj GEMV inside a decode step: besides storing the bf16
 // projection, runs the causal conv + SiLU on the xBC columns and shifts the
@@ -45,17 +37,18 @@ struct ConvEpilogue {
 };
 
 // out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda].
-// conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue.
+// conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue
+// (which needs the xBC range to start on a multiple of 32 features).
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, void* ws, hipStream_t st);
+                       const ConvEpilogue* conv, hipStream_t st);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        hipStream_t st);
 
-// ---- decode SSM update + gated group RMSNorm + out_proj quant (decode.hip)
+// ---- decode SSM state update (decode.hip)
 struct DecodeSsmArgs {
     const int32_t* slot_idx;
     float* ssm_pool;
@@ -64,16 +57,24 @@ struct DecodeSsmArgs {
     const float* A_log;
     const float* D;
     const float* dt_bias;
-    const uint16_t* norm_w;
-    const float* out_a_scale;
     uint16_t* y;               // [m, d_inner]
-    uint16_t* norm;            // [m, d_inner]
-    uint8_t* q_out;            // [m, d_inner]
-    unsigned* group_counters;  // [m * n_groups], zero between calls
-    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, z_off, dt_off, b_off, c_off;
-    float eps;
+    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, dt_off, b_off, c_off;
 };
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st);
+
+// ---- gated group RMSNorm + out_proj quant (norm.hip)
+struct GnormArgs {
+    int64_t T;
+    int32_t n_groups, d_inner, d_in_proj, z_off;
+    float eps;
+    const uint16_t* y;         // [T, d_inner]
+    const uint16_t* zxbcdt;    // [T, d_in_proj] (z columns)
+    const uint16_t* norm_w;    // [d_inner]
+    const float* out_a_scale;  // [1]
+    uint16_t* norm;            // [T, d_inner] bf16 norm output (nullptr: not kept)
+    uint8_t* q_out;            // [T, d_inner]
+};
+nhm_status launch_gnorm_quant(const GnormArgs& a, hipStream_t st);
 
 // ---- prefill pieces (prefill.hip)
 struct PrefillArgs {
@@ -104,6 +105,7 @@ struct PrefillArgs {
     uint16_t* norm;           // [T, d_inner] (nullptr: not kept)
     uint8_t* q_out;           // [T, d_inner]
 };
+// conv, chunked scan and the gated norm + quant, in stream order.
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st);
 
 }  // namespace nhm

@@ -1,0 +1,61 @@
+// Gated group RMSNorm fused with the static e4m3 quant of the out_proj input
+// ([PR1288] "What it does": RmsNormGatedGroup(n_groups) -> out_proj (FP8 W8A8)).
+//
+// One wave per (token, group): v = y * silu(z); o = bf16(v / sqrt(mean(v^2) + eps) * w);
+// q = E4M3(o / s_out). The gate is applied before the mean square; groups are
+// contiguous runs of d_inner / n_groups channels. HBM-bound: reads y and z (bf16),
+// writes o (bf16) and q (e4m3), 8 channels per lane per 16-byte load.
+#include "nhm_device.h"
+#include "nhm_internal.h"
+
+namespace nhm {
+
+__global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= a.T * a.n_groups) return;
+    const int64_t tok = pair / a.n_groups;
+    const int g = (int)(pair % a.n_groups);
+    const int gw = a.d_inner / a.n_groups;
+    const uint16_t* yr = a.y + tok * a.d_inner + (int64_t)g * gw;
+    const uint16_t* zr = a.zxbcdt + tok * a.d_in_proj + a.z_off + (int64_t)g * gw;
+    float ss = 0.f;
+    for (int c = lane * 8; c < gw; c += 64 * 8) {
+        float y[8], z[8];
+        unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
+        unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = y[j] * silu(z[j]);
+            ss += v * v;
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
+    const float so = *a.out_a_scale;
+    for (int c = lane * 8; c < gw; c += 64 * 8) {
+        float y[8], z[8], w[8];
+        unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
+        unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
+        unpack8(*reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c), w);
+        uint32_t ob[8], q[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ob[j] = f32_to_bf16(y[j] * silu(z[j]) * r * w[j]);
+            q[j >> 2] |= quant_bf16(ob[j], so) << (8 * (j & 3));
+        }
+        const int64_t o = tok * a.d_inner + (int64_t)g * gw + c;
+        if (a.norm)
+            *reinterpret_cast<uint4*>(a.norm + o) =
+                make_uint4(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16), ob[4] | (ob[5] << 16), ob[6] | (ob[7] << 16));
+        *reinterpret_cast<uint2*>(a.q_out + o) = make_uint2(q[0], q[1]);
+    }
+}
+
+nhm_status launch_gnorm_quant(const GnormArgs& a, hipStream_t st) {
+    if (a.T <= 0) return NHM_OK;
+    gnorm_quant_kernel<<<dim3((unsigned)((a.T * a.n_groups + 3) / 4)), 256, 0, st>>>(a);
+    return check_launch("gnorm_quant");
+}
+
+}  // namespace nhm

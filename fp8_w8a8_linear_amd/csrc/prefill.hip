@@ -1,10 +1,10 @@
-// Prefill kernels between the two projections: varlen causal conv, the Mamba2
-// chunked scan (state-space duality split) and the fused gated RMSNorm + e4m3
-// quant of the out_proj input.
+// Prefill kernels between the two projections: varlen causal conv and the Mamba2
+// chunked scan (state-space duality split).
 //
 // [PR1288] "What it does": in_proj -> split z | xBC | dt -> CausalConv1dFwd(silu)
 // -> split x | B | C -> Mamba2ChunkScan -> RmsNormGatedGroup(n_groups) -> out_proj.
-// The splits are column offsets into the projection rows; nothing is copied.
+// The splits are column offsets into the projection rows; nothing is copied. The
+// gated norm (norm.hip) follows the scan.
 //
 // Chunked scan (Dao & Gu 2024, "Transformers are SSMs", the SSD algorithm): chunks
 // of Q tokens start at each sequence's first token. With cs_t the cumulative
@@ -82,14 +82,6 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int n, int64_t tok) {
     return lo;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f[2 * j] = bf16_to_f32(w[j] & 0xffffu);
-        f[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-    }
-}
 
 // Window row r (0 = oldest) of sequence i before the call: the pool row or zero.
 __device__ __forceinline__ uint4 init_row(const PrefillArgs& a, int i, int r, int c8) {
@@ -454,49 +446,6 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- gated RMSNorm + quant
-
-// One wave per (token, group): v = y * silu(z); o = bf16(v / sqrt(mean v^2 + eps) * w);
-// q = E4M3(o / s_out). 8 channels per lane.
-__global__ __launch_bounds__(256) void gnorm_quant_kernel(const PrefillArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= a.T * a.n_groups) return;
-    const int64_t tok = pair / a.n_groups;
-    const int g = (int)(pair % a.n_groups);
-    const int gw = a.d_inner / a.n_groups;
-    const float so = *a.out_a_scale;
-    float ss = 0.f;
-    for (int c = lane * 8; c < gw; c += 64 * 8) {
-        float y[8], z[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.y + tok * a.d_inner + g * gw + c), y);
-        unpack8(*reinterpret_cast<const uint4*>(a.zxbcdt + tok * a.d_in_proj + a.z_off + g * gw + c), z);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float v = y[j] * silu(z[j]);
-            ss += v * v;
-        }
-    }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
-    for (int c = lane * 8; c < gw; c += 64 * 8) {
-        float y[8], z[8], w[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.y + tok * a.d_inner + g * gw + c), y);
-        unpack8(*reinterpret_cast<const uint4*>(a.zxbcdt + tok * a.d_in_proj + a.z_off + g * gw + c), z);
-        unpack8(*reinterpret_cast<const uint4*>(a.norm_w + g * gw + c), w);
-        uint32_t ob[8], q[2] = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ob[j] = f32_to_bf16(y[j] * silu(z[j]) * r * w[j]);
-            q[j >> 2] |= quant_bf16(ob[j], so) << (8 * (j & 3));
-        }
-        if (a.norm)
-            *reinterpret_cast<uint4*>(a.norm + tok * a.d_inner + g * gw + c) =
-                make_uint4(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16), ob[4] | (ob[5] << 16), ob[6] | (ob[7] << 16));
-        *reinterpret_cast<uint2*>(a.q_out + tok * a.d_inner + g * gw + c) = make_uint2(q[0], q[1]);
-    }
-}
-
 // ---------------------------------------------------------------- launcher
 
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
@@ -508,9 +457,11 @@ nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     if (a.max_chunks > 0) ssd_state_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
     if (a.n_seqs > 0) ssd_pass_kernel<<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
     if (a.max_chunks > 0) ssd_out_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
-    if (a.T > 0)
-        gnorm_quant_kernel<<<dim3((unsigned)((a.T * a.n_groups + 3) / 4)), 256, 0, st>>>(a);
-    return check_launch("prefill");
+    nhm_status s = check_launch("prefill");
+    if (s != NHM_OK || a.T == 0) return s;
+    GnormArgs ga{a.T, a.n_groups, a.d_inner, a.d_in_proj, a.z_off, a.eps, a.y, a.zxbcdt, a.norm_w, a.out_a_scale,
+                 a.norm, a.q_out};
+    return launch_gnorm_quant(ga, st);
 }
 
 }  // namespace nhm

@@ -28,9 +28,9 @@
  *     and violating it is undefined behaviour.
  *   - bf16 tensors are passed as uint16_t bit patterns, e4m3 tensors as uint8_t
  *     codes (OCP FP8 E4M3FN: largest finite 448, no infinities).
- *   - Workspaces ("ws") are caller-allocated device memory that MUST be zero-filled
- *     once when allocated. Every call leaves the workspace's synchronisation counters
- *     at zero again, so later calls need no clearing. One workspace must not be used
+ *   - Workspaces ("ws") are caller-allocated device memory (256-byte aligned) for the
+ *     intermediates of one call; their contents on entry are ignored and on return
+ *     hold the intermediates listed in nhm_ws_layout. One workspace must not be used
  *     by two calls that can run at the same time (e.g. on two streams).
  */
 #ifndef NHM_H
@@ -158,9 +158,10 @@ NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, n
  *   w      (host struct of device pointers)
  *   out    (device) bf16 [m, ld_out], ld_out >= n; must not overlap a (rows that
  *          are 8-byte aligned are stored 4 features at a time)
- *   ws     (device, zero-filled once) >= nhm_fp8_linear_workspace_bytes(m, n, k, a_type)
+ *   ws     (device) >= nhm_fp8_linear_workspace_bytes(m, n, k, a_type) bytes (0 for an
+ *          e4m3 input, where ws may be NULL)
  * m == 0 is a valid no-op. m <= 16 runs the weight-streaming GEMV, larger m the
- * tiled MFMA GEMM. Results are deterministic (no float atomics).
+ * tiled MFMA GEMM. Results are deterministic (no atomics).
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
 NHM_API nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
                           const nhm_fp8_weight* w, uint16_t* out, int64_t ld_out,
@@ -212,7 +213,7 @@ NHM_API nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t bat
  *   conv_pool (device) bf16 [n_slots, conv_width-1, conv_dim], the previous
  *             conv_width-1 pre-conv xBC rows, oldest first; updated in place
  *   out       (device) bf16 [batch, g.hidden]; must not overlap hidden
- *   ws        (device, zero-filled once) >= nhm_mixer_decode_ws_layout(...).total
+ *   ws        (device) >= nhm_mixer_decode_ws_layout(g, batch).total bytes
  * batch == 0 is a valid no-op.
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
  * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
@@ -241,8 +242,8 @@ NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_
  *               every sequence are written to its row in place (an empty fresh
  *               sequence leaves a zero row).
  *   out         (device) bf16 [n_tokens, g.hidden]; must not overlap hidden
- *   ws          (device, zero-filled once) >=
- *               nhm_mixer_prefill_ws_layout(g, n_tokens, n_seqs, chunk).total
+ *   ws          (device) >= nhm_mixer_prefill_ws_layout(g, n_tokens, n_seqs, chunk).total
+ *               bytes
  * n_tokens == 0 with n_seqs == 0 is a valid no-op.
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
  * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */

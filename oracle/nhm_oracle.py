@@ -397,13 +397,13 @@ def mixer_sequence(p, hidden_bf16, window_bf16, state_f32, g=GEOMETRY):
     y, h = ssm_scan_sequential(xv, Bv, Cv, dt, dA, p["D"],
                                np.asarray(state_f32, np.float32).astype(np.float64))  # a7
     y_bf16 = bf16_from_f64(y.reshape(T, H * P))
-    _, o_bf16 = gated_group_rmsnorm(y_bf16, z, p["norm_w"], G, g["rms_eps"])  # a8
+    o64, o_bf16 = gated_group_rmsnorm(y_bf16, z, p["norm_w"], G, g["rms_eps"])  # a8
     q_out = quantize_static(o_bf16, p["out_a_scale"])                         # a9
     out = fp8_linear(q_out, p["out_w"], p["out_w_scale"], p["out_a_scale"])   # a10
     return dict(out=out, out_bf16=bf16_from_f64(out), window=new_window,
                 state=h.astype(np.float32), state_f64=h, q_in=q_in, zxbcdt=zxbcdt,
                 xbc_conv=xbc_conv, y_bf16=y_bf16, y=y.reshape(T, H * P),
-                norm_bf16=o_bf16, q_out=q_out)
+                norm=o64, norm_bf16=o_bf16, q_out=q_out)
 
 
 def mixer_decode(p, hidden_bf16, slot_idx, ssm_pool, conv_pool, g=GEOMETRY):
@@ -444,12 +444,12 @@ def mixer_decode(p, hidden_bf16, slot_idx, ssm_pool, conv_pool, g=GEOMETRY):
         ssm_pool[s] = h.astype(np.float32)
         y64[b] = y.reshape(-1)
         y_bf16[b] = bf16_from_f64(y.reshape(-1))
-    _, o_bf16 = gated_group_rmsnorm(y_bf16, zx[:, lay["z_off"]:lay["z_off"] + lay["z_width"]],
+    o64, o_bf16 = gated_group_rmsnorm(y_bf16, zx[:, lay["z_off"]:lay["z_off"] + lay["z_width"]],
                                     p["norm_w"], G, g["rms_eps"])                                # a8
     q_out = quantize_static(o_bf16, p["out_a_scale"])                                           # a9
     o = fp8_linear(q_out, p["out_w"], p["out_w_scale"], p["out_a_scale"])                       # a10
     out[live] = o[live]
-    res.update(xbc_conv=xbc_conv, y=y64, y_bf16=y_bf16, norm_bf16=o_bf16, q_out=q_out)
+    res.update(xbc_conv=xbc_conv, y=y64, y_bf16=y_bf16, norm=o64, norm_bf16=o_bf16, q_out=q_out)
     return out, res
 
 

@@ -40,12 +40,4 @@ def zeros_ws(nbytes):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=DEV)
 
 
-def rel_max(got, ref):
-    """max |got - ref| / RMS(ref): the block-output tolerance measure."""
-    ref = np.asarray(ref, np.float64)
-    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / np.sqrt(np.mean(ref * ref)))
-
-
-def rel_l2(got, ref):
-    ref = np.asarray(ref, np.float64)
-    return float(np.linalg.norm(np.asarray(got, np.float64) - ref) / np.linalg.norm(ref))
+from oracle.parity import block_parity, rel_l2, rel_max  # noqa: E402,F401

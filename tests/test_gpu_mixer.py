@@ -1,8 +1,10 @@
 """Block parity: nhm_mixer_decode / nhm_mixer_prefill against the oracle.
 
-Bars: e4m3 bytes bit-exact (a1 on identical input; a9 on the GPU's own bf16 norm
-output, since float noise upstream decides it); block output max|d| <= 2e-2 *
-RMS(oracle f64 output); f32 state ||d||/||ref|| <= 1e-3; untouched pool rows
+Bars (tests/gpu_util.block_parity): e4m3 bytes bit-exact (a1 on identical input;
+a9 on the GPU's own bf16 norm output); block output max|d| <= 2e-2 * RMS of the
+oracle's out_proj on the same codes; gated norm output max|d| <= 2e-2 * RMS;
+a9 codes that differ from the oracle's are adjacent and rare; f32 state
+||d||/||ref|| <= 1e-3; conv windows (bf16 copies) likewise; untouched pool rows
 bit-identical. Element counts are asserted against the geometry.
 """
 import numpy as np
@@ -13,6 +15,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 TOL_OUT, TOL_STATE = 2e-2, 1e-3
+H, I = 2688, 4096
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +38,7 @@ def _gpu_decode(nhm, pd, hidden, slots, sp, cp):
     lay = nhm.decode_ws_layout(B)
     ws = zeros_ws(lay["total"])
     spd, cpd = dev(sp), dev(cp)
-    out = torch.empty((B, 2688), dtype=torch.int16, device="cuda")
+    out = torch.empty((B, H), dtype=torch.int16, device="cuda")
     nhm.mixer_decode(pd, dev(hidden), dev(slots), spd, cpd, out, ws)
     torch.cuda.synchronize()
     return host(out), host(spd), host(cpd), ws, lay
@@ -47,30 +50,31 @@ def _gpu_prefill(nhm, pd, hidden, cu, slots, has_init, sp, cp):
     lay = nhm.prefill_ws_layout(T, len(slots))
     ws = zeros_ws(lay["total"])
     spd, cpd = dev(sp), dev(cp)
-    out = torch.empty((T, 2688), dtype=torch.int16, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     nhm.mixer_prefill(pd, dev(hidden), dev(np.asarray(cu, np.int32)), dev(np.asarray(slots, np.int32)),
                       dev(np.asarray(has_init, np.int32)), spd, cpd, out, ws)
     torch.cuda.synchronize()
     return host(out), host(spd), host(cpd), ws, lay
 
 
-def _check_out(got_bits, ref, rows=None):
-    from oracle import bf16_to_f64
-    from tests.gpu_util import rel_max
-    got = bf16_to_f64(got_bits)
-    if rows is not None:
-        got, ref = got[rows], ref[rows]
-    assert got.shape == ref.shape and got.size == ref.shape[0] * 2688
-    r = rel_max(got, ref)
-    assert r <= TOL_OUT, f"block output max|d|/RMS = {r:.4g}"
-    return r
+def _parity(out, ws, lay, rows, ref_out, ref_norm, ref_q, p):
+    """Block parity on the given token rows, reading the GPU's a9 codes and norm output from ws."""
+    from tests.gpu_util import block_parity, ws_region
+    T = out.shape[0]
+    q = ws_region(ws, lay["q_out"], T * I, np.uint8).reshape(T, I)[rows]
+    nrm = ws_region(ws, lay["norm"], T * I, np.uint16).reshape(T, I)[rows]
+    o = out[rows]
+    assert o.shape == (len(rows), H) and q.shape == (len(rows), I)
+    return block_parity(o, q, nrm, ref_out[rows] if ref_out.shape[0] == T else ref_out, ref_norm, ref_q, p)
 
 
 def _check_states(sp_gpu, sp_ref, sp_before, touched):
     from tests.gpu_util import rel_l2
     worst = 0.0
     for s in range(sp_ref.shape[0]):
-        if s in touched:
+        if s in touched and not np.any(sp_ref[s]):       # a fresh empty sequence leaves zeros
+            assert not np.any(sp_gpu[s]), f"slot {s} should be zero"
+        elif s in touched:
             r = rel_l2(sp_gpu[s], sp_ref[s])
             worst = max(worst, r)
             assert r <= TOL_STATE, f"slot {s}: state rel l2 {r:.3g}"
@@ -81,18 +85,23 @@ def _check_states(sp_gpu, sp_ref, sp_before, touched):
 
 def _check_windows(cp_gpu, cp_ref, cp_before, touched):
     from oracle import bf16_to_f64
+    from tests.gpu_util import rel_l2, rel_max
     for s in range(cp_ref.shape[0]):
         if s in touched:
             a, b = bf16_to_f64(cp_gpu[s]), bf16_to_f64(cp_ref[s])
-            # copies of bf16 in_proj outputs: equal up to one bf16 rounding of the projection
-            assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30), f"slot {s} window"
+            if not np.any(b):
+                assert not np.any(a)
+                continue
+            # copies of bf16 in_proj outputs: they differ only where the f32 and the f64
+            # projection round to different bf16 neighbours
+            assert rel_l2(a, b) <= TOL_STATE and rel_max(a, b) <= TOL_OUT, f"slot {s} window"
         else:
             assert np.array_equal(cp_gpu[s], cp_before[s])
 
 
 def test_decode_one_block_one_token(nhm, block0):
     """One decode token through one block (m = 1), state from the pool."""
-    from oracle import mixer_decode, quantize_static
+    from oracle import mixer_decode
     from tests.gpu_util import upload_params, ws_region
     from workloads import conv_pool, hidden, ssm_pool
     S = 4
@@ -103,18 +112,12 @@ def test_decode_one_block_one_token(nhm, block0):
     out, spg, cpg, ws, lay = _gpu_decode(nhm, pd, h, slots, sp, cp)
     spr, cpr = sp.copy(), cp.copy()
     ref, res = mixer_decode(block0, h, slots, spr, cpr)
-    # a1: bit-exact
-    assert np.array_equal(ws_region(ws, lay["q_in"], 2688, np.uint8), res["q_in"].reshape(-1))
-    # a9: the GPU's own bf16 norm output through the oracle quantizer
-    norm = ws_region(ws, lay["norm"], 4096, np.uint16)
-    q_out = ws_region(ws, lay["q_out"], 4096, np.uint8)
-    assert np.array_equal(q_out, quantize_static(norm.reshape(1, -1), block0["out_a_scale"]).reshape(-1))
-    r = _check_out(out, ref)
+    assert np.array_equal(ws_region(ws, lay["q_in"], H, np.uint8), res["q_in"].reshape(-1))   # a1
+    m = _parity(out, ws, lay, [0], ref, res["norm"], res["q_out"], block0)
     st = _check_states(spg, spr, sp, {2})
     _check_windows(cpg, cpr, cp, {2})
-    # the two older window rows are exact shifts
-    assert np.array_equal(cpg[2][:2], cp[2][1:])
-    print(f"decode m=1: out max|d|/RMS {r:.3e}, state rel l2 {st:.3e}")
+    assert np.array_equal(cpg[2][:2], cp[2][1:])          # the two older rows shift exactly
+    print(f"decode m=1: {m}, state rel l2 {st:.3e}")
 
 
 @pytest.mark.parametrize("B,slot_list", [(8, None), (3, [5, -1, 0]), (20, None)])
@@ -127,20 +130,21 @@ def test_decode_batch(nhm, block0, B, slot_list):
     sl = np.array(slot_list, np.int32) if slot_list else slots(2, B, S)
     sp, cp = ssm_pool(2, 0, S), conv_pool(2, 0, S)
     pd = upload_params(block0)
-    out, spg, cpg, _, _ = _gpu_decode(nhm, pd, h, sl, sp, cp)
+    out, spg, cpg, ws, lay = _gpu_decode(nhm, pd, h, sl, sp, cp)
     spr, cpr = sp.copy(), cp.copy()
-    ref, _ = mixer_decode(block0, h, sl, spr, cpr)
+    ref, res = mixer_decode(block0, h, sl, spr, cpr)
     live = [b for b in range(B) if sl[b] >= 0]
-    _check_out(out, ref, rows=live)
+    m = _parity(out, ws, lay, live, ref, res["norm"][live], res["q_out"][live], block0)
     pad = [b for b in range(B) if sl[b] < 0]
     assert np.all(out[pad] == 0)
     touched = {int(s) for s in sl if s >= 0}
     _check_states(spg, spr, sp, touched)
     _check_windows(cpg, cpr, cp, touched)
+    print(f"decode B={B}: {m}")
 
 
 def test_decode_stacked_layers(nhm):
-    """Paged decode B=8 through 3 stacked blocks (the full 23 run in bench.py)."""
+    """Paged decode B=8 through 3 stacked blocks (bench.py checks layers of the full 23)."""
     from oracle import mixer_decode
     from tests.gpu_util import dev, host, upload_params, zeros_ws
     from workloads import block_params, conv_pool, hidden, slots, ssm_pool
@@ -148,20 +152,23 @@ def test_decode_stacked_layers(nhm):
     sl = slots(2, B, S)
     x = hidden(2, B)
     xd = dev(x)
-    ws = zeros_ws(nhm.decode_ws_layout(B)["total"])
+    lay = nhm.decode_ws_layout(B)
+    ws = zeros_ws(lay["total"])
     for layer in range(L):
         p = block_params(2, layer)
         sp, cp = ssm_pool(2, layer, S), conv_pool(2, layer, S)
         spd, cpd = dev(sp), dev(cp)
-        out = torch.empty((B, 2688), dtype=torch.int16, device="cuda")
+        out = torch.empty((B, H), dtype=torch.int16, device="cuda")
         nhm.mixer_decode(upload_params(p), xd, dev(sl), spd, cpd, out, ws)
         torch.cuda.synchronize()
         spr, cpr = sp.copy(), cp.copy()
-        ref, _ = mixer_decode(p, x, sl, spr, cpr)      # oracle on the same bf16 layer input
+        ref, res = mixer_decode(p, x, sl, spr, cpr)      # oracle on the same bf16 layer input
         got = host(out)
-        _check_out(got, ref)
+        m = _parity(got, ws, lay, list(range(B)), ref, res["norm"], res["q_out"], p)
         _check_states(host(spd), spr, sp, set(int(s) for s in sl))
-        x, xd = got, out                              # next layer input: this layer's bf16 output
+        _check_windows(host(cpd), cpr, cp, set(int(s) for s in sl))
+        print(f"layer {layer}: {m}")
+        x, xd = got, out                                # next layer input: this layer's bf16 output
 
 
 def test_decode_deterministic(nhm, block0):
@@ -177,6 +184,13 @@ def test_decode_deterministic(nhm, block0):
         assert np.array_equal(x, y)
 
 
+def _prefill_refs(res, lens):
+    norm = np.concatenate([r["norm"] for r, L in zip(res, lens) if L > 0])
+    q = np.concatenate([r["q_out"] for r, L in zip(res, lens) if L > 0])
+    qin = np.concatenate([r["q_in"] for r, L in zip(res, lens) if L > 0])
+    return norm, q, qin
+
+
 def test_prefill_512_one_block(nhm, block0):
     """Prefill of one 512-token sequence (4 chunks) from a carried state."""
     from oracle import mixer_prefill
@@ -190,15 +204,12 @@ def test_prefill_512_one_block(nhm, block0):
     out, spg, cpg, ws, lay = _gpu_prefill(nhm, pd, h, cu, sl, hi, sp, cp)
     spr, cpr = sp.copy(), cp.copy()
     ref, res = mixer_prefill(block0, h, cu, sl, hi, spr, cpr)
-    assert np.array_equal(ws_region(ws, lay["q_in"], T * 2688, np.uint8), res[0]["q_in"].reshape(-1))
-    from oracle import quantize_static
-    norm = ws_region(ws, lay["norm"], T * 4096, np.uint16).reshape(T, 4096)
-    q_out = ws_region(ws, lay["q_out"], T * 4096, np.uint8).reshape(T, 4096)
-    assert np.array_equal(q_out, quantize_static(norm, block0["out_a_scale"]))
-    r = _check_out(out, ref)
+    norm, q, qin = _prefill_refs(res, [T])
+    assert np.array_equal(ws_region(ws, lay["q_in"], T * H, np.uint8), qin.reshape(-1))     # a1
+    m = _parity(out, ws, lay, list(range(T)), ref, norm, q, block0)
     st = _check_states(spg, spr, sp, {1})
     _check_windows(cpg, cpr, cp, {1})
-    print(f"prefill 512: out max|d|/RMS {r:.3e}, state rel l2 {st:.3e}")
+    print(f"prefill 512: {m}, state rel l2 {st:.3e}")
 
 
 @pytest.mark.parametrize("lens,has_init", [([5, 130, 1, 0, 260, 128], [1, 0, 1, 0, 1, 0]),
@@ -214,21 +225,20 @@ def test_prefill_ragged(nhm, block0, lens, has_init):
     sp, cp = ssm_pool(4, 0, S), conv_pool(4, 0, S)
     sl = np.array([7, 0, 3, 5, 1, 6][:len(lens)], np.int32)
     pd = upload_params(block0)
-    out, spg, cpg, _, _ = _gpu_prefill(nhm, pd, h, cu, sl, has_init, sp, cp)
+    out, spg, cpg, ws, lay = _gpu_prefill(nhm, pd, h, cu, sl, has_init, sp, cp)
     spr, cpr = sp.copy(), cp.copy()
-    ref, _ = mixer_prefill(block0, h, cu, sl, has_init, spr, cpr)
-    _check_out(out, ref)
+    ref, res = mixer_prefill(block0, h, cu, sl, has_init, spr, cpr)
+    norm, q, _ = _prefill_refs(res, lens)
+    m = _parity(out, ws, lay, list(range(T)), ref, norm, q, block0)
     touched = set(int(s) for s in sl)
-    for s in touched:
-        if not np.any(spr[s]):                       # an empty fresh sequence leaves a zero row
-            assert not np.any(spg[s])
-    _check_states(spg, spr, sp, {s for s in touched if np.any(spr[s])})
+    _check_states(spg, spr, sp, touched)
     _check_windows(cpg, cpr, cp, touched)
+    print(f"prefill {lens}: {m}")
 
 
 def test_decode_equals_prefill_of_one(nhm, block0):
-    from tests.gpu_util import rel_max, upload_params
     from oracle import bf16_to_f64
+    from tests.gpu_util import rel_max, upload_params
     from workloads import conv_pool, hidden, ssm_pool
     h = hidden(0, 2)
     sp, cp = ssm_pool(0, 2, 4), conv_pool(0, 2, 4)
@@ -239,6 +249,7 @@ def test_decode_equals_prefill_of_one(nhm, block0):
     assert rel_max(bf16_to_f64(od), bf16_to_f64(op)) <= TOL_OUT
     for s in (3, 1):
         assert np.linalg.norm(spd[s] - spp[s]) <= 1e-4 * np.linalg.norm(spp[s])
+    assert np.array_equal(cpd, cpp)
 
 
 def test_prefill_carry_split(nhm, block0):
