@@ -59,8 +59,9 @@ def _lin(nhm, a, a_type, m, lda, w, out, ld_out, ws, wsb):
 
 def test_linear_refusals(nhm):
     A, O, WS = 0x10000, 0x20000, 0x40000
-    need = nhm.fp8_linear_workspace_bytes(4, 64, 128, nhm.NHM_BF16)
-    assert need >= 4 * 128
+    need = nhm.fp8_linear_workspace_bytes(32, 64, 128, nhm.NHM_BF16)
+    assert need >= 32 * 128                                  # bf16 into the GEMM: an e4m3 copy
+    assert nhm.fp8_linear_workspace_bytes(4, 64, 128, nhm.NHM_BF16) == 0   # the GEMV quantizes on chip
     cases = [
         (dict(a=None), 1), (dict(out=None), 1), (dict(w=_w(nhm, w=0)), 1),
         (dict(w=_w(nhm, k=100)), 2), (dict(w=_w(nhm, n=0)), 2), (dict(m=-1), 2), (dict(lda=64), 2),
@@ -68,7 +69,7 @@ def test_linear_refusals(nhm):
         (dict(wsb=need - 1), 5), (dict(ws=None), 5), (dict(a_type=7), 4), (dict(ws=WS + 8), 3),
     ]
     for over, status in cases:
-        kw = dict(a=A, a_type=nhm.NHM_BF16, m=4, lda=128, w=_w(nhm), out=O, ld_out=64, ws=WS, wsb=need)
+        kw = dict(a=A, a_type=nhm.NHM_BF16, m=32, lda=128, w=_w(nhm), out=O, ld_out=64, ws=WS, wsb=need)
         kw.update(over)
         st = _lin(nhm, kw["a"], kw["a_type"], kw["m"], kw["lda"], kw["w"], kw["out"], kw["ld_out"], kw["ws"], kw["wsb"])
         assert st == status, (over, st, nhm.lib.nhm_last_error())
