@@ -34,9 +34,8 @@ static nhm_status check_geometry(const nhm_geometry* g) {
     if (g->head_dim != 64 || g->d_state != 128 || g->conv_width != 4)
         return fail(NHM_ERR_UNSUPPORTED, "kernels implement head_dim 64, d_state 128, conv_width 4 (got %d, %d, %d)",
                     g->head_dim, g->d_state, g->conv_width);
-    if (g->n_heads % g->n_groups != 0 || g->n_heads / g->n_groups > 8)
-        return fail(NHM_ERR_UNSUPPORTED, "n_heads %d must be a multiple of n_groups %d, at most 8 per group",
-                    g->n_heads, g->n_groups);
+    if (g->n_heads % g->n_groups != 0)
+        return fail(NHM_ERR_UNSUPPORTED, "n_heads %d is not a multiple of n_groups %d", g->n_heads, g->n_groups);
     if (g->hidden % 16 != 0 || g->hidden > 16384)
         return fail(NHM_ERR_UNSUPPORTED, "hidden %d must be a multiple of 16 and at most 16384", g->hidden);
     if (!(g->rms_eps > 0.f) || !isfinite(g->rms_eps))
@@ -78,13 +77,9 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
 
 // ---------------------------------------------------------------- workspace layouts
 
-// The weight-streaming GEMV serves m <= 16 (quantizing a bf16 input itself); the
-// tiled GEMM the rest, after a separate quant of a bf16 input into the workspace.
-static bool use_gemv(int64_t m, int64_t k, bool bf16_in) { return gemv_supports(m, k, bf16_in); }
-
 // bytes of the e4m3 copy of a bf16 activation (the only workspace nhm_fp8_linear needs)
 static size_t linear_ws(int64_t m, int64_t k, nhm_dtype t) {
-    return t == NHM_BF16 && !use_gemv(m, k, true) ? align_up((size_t)m * (size_t)k, 256) : 0;
+    return t == NHM_BF16 ? align_up((size_t)m * (size_t)k, 256) : 0;
 }
 
 struct MixerWs {
@@ -134,11 +129,14 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     return w;
 }
 
+// The weight-streaming GEMV serves m <= 16 (and k up to 16384); the tiled GEMM the rest.
+static bool use_gemv(int64_t m, int64_t k) { return m <= 16 && k <= 16384; }
+
 // One projection on an e4m3 activation [m, lda].
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
-                          int64_t ld_out, hipStream_t st) {
-    if (use_gemv(m, w.k, false))
-        return launch_gemv(a, false, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, nullptr, nullptr, st);
+                          int64_t ld_out, const ConvEpilogue* conv, hipStream_t st) {
+    if (use_gemv(m, w.k))
+        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st);
     return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
 }
 
@@ -235,9 +233,6 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
     const uint8_t* aq = static_cast<const uint8_t*>(a);
     int64_t lda = ld_a;
     char* wsb = static_cast<char*>(ws);
-    if (a_type == NHM_BF16 && use_gemv(m, w->k, true))
-        return launch_gemv(a, true, ld_a, (int)m, w->w, w->w_scale, w->a_scale, w->n, w->k, out, ld_out, nullptr,
-                           nullptr, st);
     if (a_type == NHM_BF16) {
         uint8_t* q = reinterpret_cast<uint8_t*>(wsb);
         launch_quantize(static_cast<const uint16_t*>(a), m, w->k, ld_a, w->a_scale, q, w->k, st);
@@ -245,7 +240,7 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
         aq = q;
         lda = w->k;
     }
-    return project(aq, lda, m, *w, out, ld_out, st);
+    return project(aq, lda, m, *w, out, ld_out, nullptr, st);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
@@ -297,14 +292,13 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
     uint16_t* xc = reinterpret_cast<uint16_t*>(wsb + w.pub.xbc_conv);
     uint8_t* q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
 
-    // in_proj with the activation quant fused in front and the conv fused behind, 16 rows at a time
+    launch_quantize(hidden, batch, H, H, p->in_proj.a_scale, q_in, H, st);
+    if ((s = check_launch("decode quant")) != NHM_OK) return s;
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
         ConvEpilogue ce{slot_idx + r0, conv_pool, p->conv_w, p->conv_b, xc + (int64_t)r0 * l.conv_dim, l.xbc_off,
                         l.conv_dim};
-        s = launch_gemv(hidden + (int64_t)r0 * H, true, H, mg, p->in_proj.w, p->in_proj.w_scale, p->in_proj.a_scale,
-                        p->in_proj.n, p->in_proj.k, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce,
-                        q_in + (int64_t)r0 * H, st);
+        s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce, st);
         if (s != NHM_OK) return s;
     }
     DecodeSsmArgs da;
@@ -315,25 +309,22 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
     da.A_log = p->A_log;
     da.D = p->D;
     da.dt_bias = p->dt_bias;
-    da.norm_w = p->norm_w;
-    da.out_a_scale = p->out_proj.a_scale;
     da.y = reinterpret_cast<uint16_t*>(wsb + w.pub.y);
-    da.norm = reinterpret_cast<uint16_t*>(wsb + w.pub.norm);
-    da.q_out = q_out;
     da.n_heads = p->g.n_heads;
     da.n_groups = p->g.n_groups;
     da.d_in_proj = l.d_in_proj;
     da.conv_dim = l.conv_dim;
     da.d_inner = l.d_inner;
-    da.z_off = l.z_off;
     da.dt_off = l.dt_off;
     da.b_off = l.b_off;
     da.c_off = l.c_off;
-    da.eps = p->g.rms_eps;
     if ((s = launch_decode_ssm(da, batch, st)) != NHM_OK) return s;
+    GnormArgs ga{batch, p->g.n_groups, l.d_inner, l.d_in_proj, l.z_off, p->g.rms_eps, da.y, zx, p->norm_w,
+                 p->out_proj.a_scale, reinterpret_cast<uint16_t*>(wsb + w.pub.norm), q_out};
+    if ((s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, st);
+        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, nullptr, st);
         if (s != NHM_OK) return s;
     }
     return NHM_OK;
@@ -373,7 +364,7 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     if (n_tokens > 0) {
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
-        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, st)) != NHM_OK) return s;
+        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, st)) != NHM_OK) return s;
     }
     PrefillArgs a;
     a.T = n_tokens;
@@ -415,7 +406,7 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     a.q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
     if ((s = launch_prefill_mid(a, st)) != NHM_OK) return s;
     if (n_tokens > 0)
-        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, st);
+        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, nullptr, st);
     return NHM_OK;
 }
 

@@ -36,21 +36,19 @@ struct ConvEpilogue {
     int32_t conv_dim;
 };
 
-// out[m, n] = bf16(sum_k a_q[m,k] w[n,k] * a_scale * w_scale[n]). a is e4m3 [m, lda], or,
-// with bf16_in, bf16 [m, lda] quantized with a_scale inside the kernel (q_copy, if not
-// null, receives those e4m3 codes as [m, k]). conv == nullptr: plain store to
-// out[m * ld_out + n]; otherwise also the conv epilogue.
-bool gemv_supports(int64_t m, int64_t k, bool bf16_in);
-nhm_status launch_gemv(const void* a, bool bf16_in, int64_t lda, int m, const uint8_t* w, const float* w_scale,
+// out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda].
+// conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue
+// (which needs the xBC range to start on a multiple of 32 features).
+nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, uint8_t* q_copy, hipStream_t st);
+                       const ConvEpilogue* conv, hipStream_t st);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        hipStream_t st);
 
-// ---- decode: SSM state update + gated group RMSNorm + out_proj quant (decode.hip)
+// ---- decode SSM state update (decode.hip)
 struct DecodeSsmArgs {
     const int32_t* slot_idx;
     float* ssm_pool;
@@ -59,13 +57,8 @@ struct DecodeSsmArgs {
     const float* A_log;
     const float* D;
     const float* dt_bias;
-    const uint16_t* norm_w;    // [d_inner]
-    const float* out_a_scale;  // [1]
     uint16_t* y;               // [m, d_inner]
-    uint16_t* norm;            // [m, d_inner]
-    uint8_t* q_out;            // [m, d_inner]
-    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, z_off, dt_off, b_off, c_off;
-    float eps;
+    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, dt_off, b_off, c_off;
 };
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st);
 
