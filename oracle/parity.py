@@ -29,11 +29,12 @@ def block_parity(out_bits, q_gpu, norm_gpu, ref_out, ref_norm, ref_q, p, tol=2e-
       3. the bf16 norm output against the oracle's float64 one: ||d|| / ||ref|| <=
          4e-3 (one bf16 ulp) and |d| <= 2^-7 |ref| + 0.05 RMS elementwise;
       4. every code that differs from the oracle's is reachable from a norm value
-         within eta = 2^-7 |o| + 0.02 RMS of the oracle's o, and such codes are
+         within eta = 2^-7 |o| + 0.05 RMS of the oracle's o (the elementwise norm bound), and such codes are
          rare (<= 1 %).
     Bounds 3-4 are the float-noise floor: evaluating the oracle with float32
     accumulation in its projections (the pages' COMPUTE_32F) moves its own norm
-    output by up to 0.017 RMS before rounding and flips ~0.03 % of its a9 codes.
+    output by up to 0.025 RMS before rounding and flips ~0.03 % of its a9 codes
+    (tests/test_oracle_noise_floor.py).
     The end-to-end difference to the oracle's output is returned and held to a
     sanity bound only: the same float32 variant of the oracle already differs
     from the float64 oracle by 0.0206 RMS end to end at T = 128.
@@ -56,7 +57,7 @@ def block_parity(out_bits, q_gpu, norm_gpu, ref_out, ref_norm, ref_q, p, tol=2e-
     assert frac <= 0.01, f"{frac:.4%} of the a9 codes differ from the oracle's"
     if diff.any():
         o = ref_norm[diff]
-        eta = 2.0 ** -7 * np.abs(o) + 0.02 * rms_n
+        eta = 2.0 ** -7 * np.abs(o) + 0.05 * rms_n
         lo = e4m3_decode(quantize_static(bf16_from_f64(o - eta), s))
         hi = e4m3_decode(quantize_static(bf16_from_f64(o + eta), s))
         qv = e4m3_decode(q_gpu[diff])
