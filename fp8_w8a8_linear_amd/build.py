@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnhm.so")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "decode.hip", "norm.hip", "prefill.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "decode.hip", "norm.hip", "prefill.hip", "ssd.hip"]
 
 
 def hipcc():

@@ -108,4 +108,9 @@ struct PrefillArgs {
 // conv, chunked scan and the gated norm + quant, in stream order.
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st);
 
+// SSD chunk kernels on the bf16 MFMA (ssd.hip): per (chunk, head) dt, cumulative
+// log-decay and the chunk's own state; then, after the state pass, the outputs.
+void launch_ssd_state(const PrefillArgs& a, hipStream_t st);
+void launch_ssd_out(const PrefillArgs& a, hipStream_t st);
+
 }  // namespace nhm

@@ -14,7 +14,8 @@
 //                  seeded from the pool row (or zero) and written back in place
 //   output kernel: y_t = sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s
 //                        + exp(cs_t) C_t . H_in(c) + D x_t
-// All three run in f32 on the VALU with LDS-staged operands.
+// The state and output kernels (ssd.hip) run the contractions on the bf16 MFMA;
+// the pass kernel below is a sequential f32 walk over the chunks of a sequence.
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -170,91 +171,6 @@ __global__ __launch_bounds__(256) void conv_store_kernel(const PrefillArgs a) {
     for (int r = 0; r < 3; ++r) dst[(int64_t)r * a.conv_dim / 8] = v[r];
 }
 
-// ---------------------------------------------------------------- SSD: chunk states
-
-// One workgroup per (chunk, head): dt, cumulative log-decay and the chunk's own
-// state contribution S_c[p][n] (zero initial state).
-__global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
-    const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-    const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
-    if (info.x < 0) return;
-    const int64_t tok0 = info.y;
-    const int L = info.z;
-    const int g = h / (a.n_heads / a.n_groups);
-    __shared__ float s_cs[kQ], s_dt[kQ];
-    __shared__ __attribute__((aligned(16))) float s_x[kQ][kHP];   // w_s * x_s
-    __shared__ __attribute__((aligned(16))) float s_b[kQ][kDS];
-
-    const float A = -__expf(a.A_log[h]);
-    if (t < kQ) {
-        float dt = 0.f;
-        if (t < L) dt = softplus(bf16_to_f32(a.zxbcdt[(tok0 + t) * a.d_in_proj + a.dt_off + h]) + a.dt_bias[h]);
-        s_dt[t] = dt;
-        s_cs[t] = dt * A;
-    }
-    __syncthreads();
-    for (int o = 1; o < kQ; o <<= 1) {        // inclusive scan of dt*A over the chunk
-        float add = 0.f;
-        if (t < kQ && t >= o) add = s_cs[t - o];
-        __syncthreads();
-        if (t < kQ) s_cs[t] += add;
-        __syncthreads();
-    }
-    const float cs_end = s_cs[L - 1];
-    float* cs_out = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
-    float* dt_out = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
-    if (t < kQ) {
-        cs_out[t] = s_cs[t];
-        dt_out[t] = s_dt[t];
-    }
-    // stage w_s x_s and B_s (zero rows beyond L)
-    for (int e = t; e < kQ * kHP / 8; e += 256) {
-        const int s = e / (kHP / 8), p8 = e % (kHP / 8);
-        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (s < L) {
-            unpack8(*reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8), f);
-            const float ws = __expf(cs_end - s_cs[s]) * s_dt[s];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[j] *= ws;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s_x[s][p8 * 8 + j] = f[j];
-    }
-    for (int e = t; e < kQ * kDS / 8; e += 256) {
-        const int s = e / (kDS / 8), n8 = e % (kDS / 8);
-        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (s < L) unpack8(*reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + a.b_off + g * kDS + n8 * 8), f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s_b[s][n8 * 8 + j] = f[j];
-    }
-    __syncthreads();
-    // thread: p = 4*(t/16) .. +3, n = 8*(t%16) .. +7
-    const int p0 = 4 * (t >> 4), n0 = 8 * (t & 15);
-    float acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-    for (int s = 0; s < L; ++s) {
-        const float4 xv = *reinterpret_cast<const float4*>(&s_x[s][p0]);
-        const float4 b0 = *reinterpret_cast<const float4*>(&s_b[s][n0]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&s_b[s][n0 + 4]);
-        const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        const float bs[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xs[i], bs[j], acc[i][j]);
-    }
-    float* out = a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4* o = reinterpret_cast<float4*>(out + (p0 + i) * kDS + n0);
-        o[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-        o[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
-    }
-}
-
 // ---------------------------------------------------------------- SSD: state passing
 
 // One workgroup per (sequence, head, block of 8 state rows). Walks the sequence's
@@ -285,167 +201,6 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
     *pool = H;
 }
 
-// ---------------------------------------------------------------- SSD: chunk outputs
-
-// LDS swizzles of the output kernel. Threads of a wave read rows that are 4 or 8
-// apart; XOR-ing the 16-byte chunk index with the row's block index spreads
-// those rows over the banks.
-__device__ __forceinline__ int sw_bf(int row, int col) {      // bf16 [128][128]
-    return row * kDS + ((((col >> 3) ^ (row >> 3)) & 15) << 3) + (col & 7);
-}
-__device__ __forceinline__ int sw_g(int row, int col) {       // f32 [128][128]
-    return row * kQ + ((((col >> 2) ^ (row >> 3)) & 31) << 2) + (col & 3);
-}
-__device__ __forceinline__ int sw_h(int row, int col) {       // f32 [64][128]
-    return row * kDS + ((((col >> 2) ^ (row >> 2)) & 31) << 2) + (col & 3);
-}
-
-// One workgroup per (chunk, head): y for the chunk's tokens.
-__global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
-    const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-    const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
-    if (info.x < 0) return;
-    const int64_t tok0 = info.y;
-    const int L = info.z;
-    const int g = h / (a.n_heads / a.n_groups);
-    __shared__ __attribute__((aligned(16))) uint16_t s_c[kQ * kDS];       // C_t, bf16 (sw_bf)
-    __shared__ __attribute__((aligned(16))) float s_bh[kQ * kDS / 2];     // B_s bf16 (sw_bf), then H_in f32 (sw_h)
-    __shared__ __attribute__((aligned(16))) float s_g[kQ * kQ];           // decayed, masked C.B * dt (sw_g)
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[kQ][kHP];
-    __shared__ float s_cs[kQ], s_dt[kQ];
-    uint16_t* s_b = reinterpret_cast<uint16_t*>(s_bh);
-
-    const float* cs_in = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
-    const float* dt_in = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
-    if (t < kQ) {
-        s_cs[t] = t < L ? cs_in[t] : 0.f;
-        s_dt[t] = t < L ? dt_in[t] : 0.f;
-    }
-    for (int e = t; e < kQ * kDS / 8; e += 256) {
-        const int s = e / (kDS / 8), n8 = e % (kDS / 8);
-        uint4 cv = make_uint4(0u, 0u, 0u, 0u), bv = cv;
-        if (s < L) {
-            const uint16_t* row = a.xbc_conv + (tok0 + s) * a.conv_dim + g * kDS + n8 * 8;
-            bv = *reinterpret_cast<const uint4*>(row + a.b_off);
-            cv = *reinterpret_cast<const uint4*>(row + a.c_off);
-        }
-        *reinterpret_cast<uint4*>(&s_b[sw_bf(s, n8 * 8)]) = bv;
-        *reinterpret_cast<uint4*>(&s_c[sw_bf(s, n8 * 8)]) = cv;
-    }
-    for (int e = t; e < kQ * kHP / 8; e += 256) {
-        const int s = e / (kHP / 8), p8 = e % (kHP / 8);
-        uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-        if (s < L) xv = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8);
-        *reinterpret_cast<uint4*>(&s_x[s][p8 * 8]) = xv;
-    }
-    __syncthreads();
-
-    // G[t][s] for t in 8*(t/16).., s in 8*(t%16)..
-    {
-        const int tb = 8 * (t >> 4), sb = 8 * (t & 15);
-        float acc[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-        if (sb <= tb + 7) {
-            for (int n2 = 0; n2 < kDS / 2; ++n2) {      // two state columns per step
-                uint32_t cw[8], bw[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(&s_c[sw_bf(tb + i, 2 * n2)]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) bw[j] = *reinterpret_cast<const uint32_t*>(&s_b[sw_bf(sb + j, 2 * n2)]);
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    float cf[8], bf[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) cf[i] = bf16_to_f32(k ? cw[i] >> 16 : cw[i] & 0xffffu);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) bf[j] = bf16_to_f32(k ? bw[j] >> 16 : bw[j] & 0xffffu);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(cf[i], bf[j], acc[i][j]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int tt = tb + i;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int ss = sb + j;
-                s_g[sw_g(tt, ss)] = (ss <= tt) ? acc[i][j] * __expf(s_cs[tt] - s_cs[ss]) * s_dt[ss] : 0.f;
-            }
-        }
-    }
-    __syncthreads();
-    // H_in(c) replaces B in LDS
-    {
-        const float4* hin = reinterpret_cast<const float4*>(a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS);
-        for (int e = t; e < kHP * kDS / 4; e += 256)
-            *reinterpret_cast<float4*>(&s_bh[sw_h(e / (kDS / 4), (e % (kDS / 4)) * 4)]) = hin[e];
-    }
-    __syncthreads();
-
-    // y[t][p] for t in 8*(t/16).., p in 4*(t%16)..
-    const int tb = 8 * (t >> 4), p0 = 4 * (t & 15);
-    float acc1[8][4], acc2[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc1[i][j] = acc2[i][j] = 0.f;
-    const int smax = min(tb + 8, L);
-    for (int s = 0; s < smax; s += 4) {
-        float gv[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = *reinterpret_cast<const float4*>(&s_g[sw_g(tb + i, s)]);
-            gv[i][0] = v.x; gv[i][1] = v.y; gv[i][2] = v.z; gv[i][3] = v.w;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[s + k][p0]);
-            const float xs[4] = {bf16_to_f32(xv.x & 0xffffu), bf16_to_f32(xv.x >> 16), bf16_to_f32(xv.y & 0xffffu),
-                                 bf16_to_f32(xv.y >> 16)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc1[i][j] = fmaf(gv[i][k], xs[j], acc1[i][j]);
-        }
-    }
-    for (int n8 = 0; n8 < kDS / 8; ++n8) {
-        float cf[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) unpack8(*reinterpret_cast<const uint4*>(&s_c[sw_bf(tb + i, n8 * 8)]), cf[i]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 h0 = *reinterpret_cast<const float4*>(&s_bh[sw_h(p0 + j, n8 * 8)]);
-            const float4 h1 = *reinterpret_cast<const float4*>(&s_bh[sw_h(p0 + j, n8 * 8 + 4)]);
-            const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc2[i][j] = fmaf(cf[i][k], hv[k], acc2[i][j]);
-        }
-    }
-    const float Dh = a.D[h];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tt = tb + i;
-        if (tt >= L) break;
-        const float e = __expf(s_cs[tt]);
-        const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[tt][p0]);
-        const float xs[4] = {bf16_to_f32(xv.x & 0xffffu), bf16_to_f32(xv.x >> 16), bf16_to_f32(xv.y & 0xffffu),
-                             bf16_to_f32(xv.y >> 16)};
-        uint32_t ob[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ob[j] = f32_to_bf16(acc1[i][j] + e * acc2[i][j] + Dh * xs[j]);
-        *reinterpret_cast<uint2*>(a.y + (tok0 + tt) * a.d_inner + h * kHP + p0) =
-            make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
-    }
-}
-
 // ---------------------------------------------------------------- launcher
 
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
@@ -454,9 +209,9 @@ nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     if (a.T > 0)
         conv_fwd_kernel<<<dim3(c8_blocks, (unsigned)((a.T + kConvRun - 1) / kConvRun)), 256, 0, st>>>(a);
     if (a.n_seqs > 0) conv_store_kernel<<<dim3(c8_blocks, a.n_seqs), 256, 0, st>>>(a);
-    if (a.max_chunks > 0) ssd_state_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
+    if (a.max_chunks > 0) launch_ssd_state(a, st);
     if (a.n_seqs > 0) ssd_pass_kernel<<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
-    if (a.max_chunks > 0) ssd_out_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
+    if (a.max_chunks > 0) launch_ssd_out(a, st);
     nhm_status s = check_launch("prefill");
     if (s != NHM_OK || a.T == 0) return s;
     GnormArgs ga{a.T, a.n_groups, a.d_inner, a.d_in_proj, a.z_off, a.eps, a.y, a.zxbcdt, a.norm_w, a.out_a_scale,
