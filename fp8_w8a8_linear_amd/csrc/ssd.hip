@@ -7,15 +7,17 @@
 //                  y_t[p]   = sum_s G[t][s] x_s[p] + exp(cs_t) sum_n C_t[n] H_in[p][n] + D x_t[p]
 // x, B and C are bf16 already (conv outputs) and enter the MFMA exactly. The
 // decay-weighted operands (w_s x_s, G, H_in) are f32; each is split into
-// bf16 hi + lo (hi = rne(v), lo = rne(v - hi), ~16 significant bits together) and
-// contracted twice, keeping the f32 state well inside its 1e-3 bound where a
-// single bf16 operand would not. Accumulation is f32.
+// bf16 hi + lo (hi = rne(v), lo = rne(v - hi): ~16 significant bits together, with
+// the hardware's packed f32 -> bf16 conversion) and contracted twice, keeping the
+// f32 state well inside its 1e-3 bound where a single bf16 operand would not.
+// Accumulation is f32.
 //
 // MFMA 16x16x32 bf16: lane l supplies row (l % 16) of A and column (l % 16) of B,
-// each as the 8 k-values 8*(l/16) .. +7 of the 32-k step (any assignment shared
-// by A and B gives the same dot products); the accumulator lane l, register r
-// holds D[4*(l/16)+r][l%16]. Both operands must be k-contiguous in LDS: C and B
-// are staged as stored ([token][state]); x and B^T are transposed while staging.
+// each as 8 k-values chosen by l / 16 (any assignment shared by A and B gives the
+// same dot products); the accumulator lane l, register r holds D[4*(l/16)+r][l%16].
+// Operands must be k-contiguous per lane. C and B rows ([token][state]) and H_in
+// ([p][n]) are; x and B^T (k = token) are transposed while staging into LDS, with
+// consecutive lanes on consecutive tokens so the 2-byte LDS writes do not conflict.
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -26,7 +28,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kHP = 64;    // head_dim
 constexpr int kDS = 128;   // d_state
 constexpr int kQ = 128;    // chunk length
-constexpr int kLd = 136;   // LDS row stride in bf16 (272 bytes: 16-byte aligned, rows 8 apart spread over the banks)
+constexpr int kLd = 136;   // LDS row stride in bf16 (272 bytes: 16-byte aligned rows)
+constexpr int kThreads = 512;
 
 __device__ __forceinline__ v4f mfma_bf16(const bf16x8& a, const bf16x8& b, const v4f& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -34,12 +37,13 @@ __device__ __forceinline__ v4f mfma_bf16(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// v = hi + lo with hi = rne_bf16(v), lo = rne_bf16(v - hi)
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-    const uint32_t h = f32_to_bf16(v);
-    hi = (uint16_t)h;
-    lo = (uint16_t)f32_to_bf16(v - bf16_to_f32(h));
+// v = hi + lo, hi = rne_bf16(v), lo = rne_bf16(v - hi)
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
 }
+
+__device__ __forceinline__ uint16_t bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
 
 // dt_s = softplus(dt_raw + bias) and the inclusive scan cs_s of dt_s * A over the
 // chunk (zero dt beyond L), in s_dt / s_cs; also stored for the other kernels.
@@ -69,7 +73,7 @@ __device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, 
 
 // ---------------------------------------------------------------- chunk states
 
-__global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void ssd_state_kernel(const PrefillArgs a) {
     const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
     if (info.x < 0) return;
@@ -84,8 +88,8 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
     chunk_decay(a, c, h, tok0, L, s_dt, s_cs);
     __syncthreads();
     const float cs_end = s_cs[L - 1];
-    for (int e = t; e < kQ * (kHP / 8); e += 256) {
-        const int s = e >> 3, p8 = e & 7;
+    for (int e = t; e < kQ * (kHP / 8); e += kThreads) {
+        const int s = e & (kQ - 1), p8 = e >> 7;
         float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (s < L) {
             unpack8(*reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8), f);
@@ -94,10 +98,15 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
             for (int j = 0; j < 8; ++j) f[j] *= ws;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) split_bf16(f[j], s_xh[(p8 * 8 + j) * kLd + s], s_xl[(p8 * 8 + j) * kLd + s]);
+        for (int j = 0; j < 8; ++j) {
+            __bf16 hi, lo;
+            split_bf16(f[j], hi, lo);
+            s_xh[(p8 * 8 + j) * kLd + s] = bits(hi);
+            s_xl[(p8 * 8 + j) * kLd + s] = bits(lo);
+        }
     }
-    for (int e = t; e < kQ * (kDS / 8); e += 256) {
-        const int s = e >> 4, n8 = e & 15;
+    for (int e = t; e < kQ * (kDS / 8); e += kThreads) {
+        const int s = e & (kQ - 1), n8 = e >> 7;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -109,39 +118,38 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(const PrefillArgs a) {
     }
     __syncthreads();
 
-    // S[p][n]: 4 p-tiles x 8 n-tiles; wave w owns n-tiles 2w, 2w+1
+    // S[p][n]: 4 p-tiles x 8 n-tiles; wave w owns n-tile w
     const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
     const int nks = (L + 31) / 32;
-    v4f acc[4][2];
+    v4f acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int ks = 0; ks < nks; ++ks) {
         const int koff = ks * 32 + q * 8;
-        const bf16x8 b0 = lds8(&s_bt[(16 * (2 * wave) + r16) * kLd + koff]);
-        const bf16x8 b1 = lds8(&s_bt[(16 * (2 * wave + 1) + r16) * kLd + koff]);
+        const bf16x8 b0 = lds8(&s_bt[(16 * wave + r16) * kLd + koff]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16x8 ah = lds8(&s_xh[(16 * i + r16) * kLd + koff]);
-            const bf16x8 al = lds8(&s_xl[(16 * i + r16) * kLd + koff]);
-            acc[i][0] = mfma_bf16(ah, b0, acc[i][0]);
-            acc[i][0] = mfma_bf16(al, b0, acc[i][0]);
-            acc[i][1] = mfma_bf16(ah, b1, acc[i][1]);
-            acc[i][1] = mfma_bf16(al, b1, acc[i][1]);
+            acc[i] = mfma_bf16(lds8(&s_xh[(16 * i + r16) * kLd + koff]), b0, acc[i]);
+            acc[i] = mfma_bf16(lds8(&s_xl[(16 * i + r16) * kLd + koff]), b0, acc[i]);
         }
     }
     float* out = a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out[(16 * i + 4 * q + r) * kDS + 16 * (2 * wave + jj) + r16] = acc[i][jj][r];
+        for (int r = 0; r < 4; ++r) out[(16 * i + 4 * q + r) * kDS + 16 * wave + r16] = acc[i][r];
 }
 
 // ---------------------------------------------------------------- chunk outputs
 
-__global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
+// One workgroup of 8 waves per (chunk, head); wave w computes the output rows of
+// t-tile w. B, H_in (split hi | lo) and x^T are staged once per workgroup; the C
+// rows of a wave's t-tile are read from L2 into registers and serve as the B
+// operand of C.B^T and the A operand of C.H_in^T. G never leaves registers: C.B^T
+// is computed transposed (B as the A operand), so a lane holds G for one row t and
+// four consecutive s of each 16-wide s-tile -- an A operand of G.x once x is read
+// for the same eight s.
+__global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) {
     const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
     if (info.x < 0) return;
@@ -149,11 +157,10 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
     const int L = info.z;
     const int g = h / (a.n_heads / a.n_groups);
     __shared__ float s_cs[kQ], s_dt[kQ];
-    __shared__ __attribute__((aligned(16))) uint16_t s_c[kQ * kLd];        // C [t][n]
-    __shared__ __attribute__((aligned(16))) uint16_t s_bh[kQ * kLd];       // B [s][n]; then H_in hi | lo [p][n]
     __shared__ __attribute__((aligned(16))) uint16_t s_xt[kHP * kLd];      // x^T [p][s]
-    __shared__ __attribute__((aligned(16))) uint16_t s_gh[kQ * kLd];       // G hi [t][s]
-    __shared__ __attribute__((aligned(16))) uint16_t s_gl[kQ * kLd];       // G lo [t][s]
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[kQ * kLd];        // B [s][n]
+    __shared__ __attribute__((aligned(16))) uint16_t s_hh[kHP * kLd];      // H_in hi [p][n]
+    __shared__ __attribute__((aligned(16))) uint16_t s_hl[kHP * kLd];      // H_in lo [p][n]
 
     const float* cs_in = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
     const float* dt_in = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
@@ -161,19 +168,8 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
         s_cs[t] = cs_in[t];
         s_dt[t] = dt_in[t];
     }
-    for (int e = t; e < kQ * (kDS / 8); e += 256) {
-        const int s = e >> 4, n8 = e & 15;
-        uint4 cv = make_uint4(0u, 0u, 0u, 0u), bv = cv;
-        if (s < L) {
-            const uint16_t* row = a.xbc_conv + (tok0 + s) * a.conv_dim + g * kDS + n8 * 8;
-            bv = *reinterpret_cast<const uint4*>(row + a.b_off);
-            cv = *reinterpret_cast<const uint4*>(row + a.c_off);
-        }
-        *reinterpret_cast<uint4*>(&s_bh[s * kLd + n8 * 8]) = bv;
-        *reinterpret_cast<uint4*>(&s_c[s * kLd + n8 * 8]) = cv;
-    }
-    for (int e = t; e < kQ * (kHP / 8); e += 256) {
-        const int s = e >> 3, p8 = e & 7;
+    for (int e = t; e < kQ * (kHP / 8); e += kThreads) {
+        const int s = e & (kQ - 1), p8 = e >> 7;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -183,100 +179,116 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(const PrefillArgs a) {
             s_xt[(p8 * 8 + 2 * j + 1) * kLd + s] = (uint16_t)(w[j] >> 16);
         }
     }
-    __syncthreads();
-
-    const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
-    // t-tiles {wave, 7 - wave}: equal shares of the lower triangle
-    const int tt[2] = {wave, 7 - wave};
-
-    // ---- G = (C B^T) * decay * dt on the lower triangle (plus the zero tile right of
-    // the diagonal that the 32-wide k-steps of the next contraction reach)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int ti = tt[u];
-        const int sj_end = ti + 1 < 7 ? ti + 1 : 7;
-        for (int sj = 0; sj <= sj_end; ++sj) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            if (sj <= ti) {
-#pragma unroll
-                for (int kn = 0; kn < kDS / 32; ++kn) {
-                    const int koff = kn * 32 + q * 8;
-                    acc = mfma_bf16(lds8(&s_c[(16 * ti + r16) * kLd + koff]), lds8(&s_bh[(16 * sj + r16) * kLd + koff]), acc);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * ti + 4 * q + r, sc = 16 * sj + r16;
-                const float v = (sc <= tr && tr < L) ? acc[r] * __expf(s_cs[tr] - s_cs[sc]) * s_dt[sc] : 0.f;
-                split_bf16(v, s_gh[tr * kLd + sc], s_gl[tr * kLd + sc]);
-            }
-        }
+    for (int e = t; e < kQ * (kDS / 8); e += kThreads) {
+        const int s = e >> 4, n8 = e & 15;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
+        *reinterpret_cast<uint4*>(&s_b[s * kLd + n8 * 8]) = v;
     }
-    __syncthreads();
-
-    // ---- H_in (the state entering this chunk, f32 [p][n]) -> hi | lo in place of B
-    uint16_t* s_hh = s_bh;
-    uint16_t* s_hl = s_bh + kHP * kLd;
     {
         const float4* hin = reinterpret_cast<const float4*>(a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS);
-        for (int e = t; e < kHP * kDS / 4; e += 256) {
+        for (int e = t; e < kHP * kDS / 4; e += kThreads) {
             const int p = e >> 5, n4 = (e & 31) * 4;
             const float4 v = hin[e];
-            uint16_t hi[4], lo[4];
+            __bf16 hi[4], lo[4];
             split_bf16(v.x, hi[0], lo[0]);
             split_bf16(v.y, hi[1], lo[1]);
             split_bf16(v.z, hi[2], lo[2]);
             split_bf16(v.w, hi[3], lo[3]);
             *reinterpret_cast<uint2*>(&s_hh[p * kLd + n4]) =
-                make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+                make_uint2(bits(hi[0]) | ((uint32_t)bits(hi[1]) << 16), bits(hi[2]) | ((uint32_t)bits(hi[3]) << 16));
             *reinterpret_cast<uint2*>(&s_hl[p * kLd + n4]) =
-                make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+                make_uint2(bits(lo[0]) | ((uint32_t)bits(lo[1]) << 16), bits(lo[2]) | ((uint32_t)bits(lo[3]) << 16));
         }
     }
     __syncthreads();
 
-    // ---- y tiles: t-tiles {wave, 7 - wave} x 4 p-tiles
-    const float Dh = a.D[h];
-    const int nks_l = (L + 31) / 32;
+    const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
+    const int ti = wave;
+    if (16 * ti >= L) return;
+    const int trow = 16 * ti + r16;                   // this lane's row t
+    const bool tok = trow < L;
+    const uint16_t* crow = a.xbc_conv + (tok0 + trow) * a.conv_dim + a.c_off + g * kDS + q * 8;
+    bf16x8 cop[kDS / 32];                             // C[t][k-step]
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int ti = tt[u];
-        if (16 * ti >= L) continue;
-        int nks = (16 * ti + 15) / 32 + 1;
-        if (nks > nks_l) nks = nks_l;
-        for (int pj = 0; pj < 4; ++pj) {
-            v4f acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks < nks; ++ks) {
-                const int koff = ks * 32 + q * 8;
-                const bf16x8 xb = lds8(&s_xt[(16 * pj + r16) * kLd + koff]);
-                acc1 = mfma_bf16(lds8(&s_gh[(16 * ti + r16) * kLd + koff]), xb, acc1);
-                acc1 = mfma_bf16(lds8(&s_gl[(16 * ti + r16) * kLd + koff]), xb, acc1);
-            }
+    for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = tok ? *reinterpret_cast<const bf16x8*>(crow + kn * 32) : bf16x8{};
+    const float cs_t = s_cs[trow];
+
+    v4f acc1[4], acc2[4];
 #pragma unroll
-            for (int kn = 0; kn < kDS / 32; ++kn) {
-                const int koff = kn * 32 + q * 8;
-                const bf16x8 ca = lds8(&s_c[(16 * ti + r16) * kLd + koff]);
-                acc2 = mfma_bf16(ca, lds8(&s_hh[(16 * pj + r16) * kLd + koff]), acc2);
-                acc2 = mfma_bf16(ca, lds8(&s_hl[(16 * pj + r16) * kLd + koff]), acc2);
+    for (int pj = 0; pj < 4; ++pj) acc1[pj] = acc2[pj] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // y1 = G x over the 32-wide s blocks kk with 32 kk <= 16 ti + 15
+    const int nkk = (16 * ti + 15) / 32 + 1;
+    for (int kk = 0; kk < nkk; ++kk) {
+        float gv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int sj = 2 * kk + half;               // s-tile
+            v4f cb = {0.f, 0.f, 0.f, 0.f};
+            if (sj <= ti) {
+#pragma unroll
+                for (int kn = 0; kn < kDS / 32; ++kn)
+                    cb = mfma_bf16(lds8(&s_b[(16 * sj + r16) * kLd + kn * 32 + q * 8]), cop[kn], cb);
             }
+            // cb[r] = (C.B^T)[t = trow][s = 16 sj + 4 q + r]
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * ti + 4 * q + r, pc = 16 * pj + r16;
-                if (tr >= L) continue;
-                const float xv = bf16_to_f32(s_xt[pc * kLd + tr]);
-                const float yv = acc1[r] + __expf(s_cs[tr]) * acc2[r] + Dh * xv;
-                a.y[(tok0 + tr) * a.d_inner + h * kHP + pc] = (uint16_t)f32_to_bf16(yv);
+                const int sc = 16 * sj + 4 * q + r;
+                gv[4 * half + r] = (sc <= trow && tok) ? cb[r] * __expf(cs_t - s_cs[sc]) * s_dt[sc] : 0.f;
             }
+        }
+        bf16x8 gh, gl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __bf16 hi, lo;
+            split_bf16(gv[j], hi, lo);
+            gh[j] = hi;
+            gl[j] = lo;
+        }
+        // B operand: x[s][p] for the same eight s, p = 16 pj + r16
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) {
+            const uint16_t* xr = &s_xt[(16 * pj + r16) * kLd + 32 * kk + 4 * q];
+            const uint2 lo = *reinterpret_cast<const uint2*>(xr);
+            const uint2 hi = *reinterpret_cast<const uint2*>(xr + 16);
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            acc1[pj] = mfma_bf16(gh, xb, acc1[pj]);
+            acc1[pj] = mfma_bf16(gl, xb, acc1[pj]);
+        }
+    }
+    // y2 = C H_in^T
+#pragma unroll
+    for (int pj = 0; pj < 4; ++pj) {
+#pragma unroll
+        for (int kn = 0; kn < kDS / 32; ++kn) {
+            const int off = (16 * pj + r16) * kLd + kn * 32 + q * 8;
+            acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hh[off]), acc2[pj]);
+            acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hl[off]), acc2[pj]);
+        }
+    }
+    // acc[r] = Y[t = 16 ti + 4 q + r][p = 16 pj + r16]
+    const float Dh = a.D[h];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * ti + 4 * q + r;
+        if (tr >= L) continue;
+        const float e = __expf(s_cs[tr]);
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) {
+            const int pc = 16 * pj + r16;
+            const float xv = bf16_to_f32(s_xt[pc * kLd + tr]);
+            a.y[(tok0 + tr) * a.d_inner + h * kHP + pc] = (uint16_t)f32_to_bf16(acc1[pj][r] + e * acc2[pj][r] + Dh * xv);
         }
     }
 }
 
 void launch_ssd_state(const PrefillArgs& a, hipStream_t st) {
-    ssd_state_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
+    ssd_state_kernel<<<dim3(a.max_chunks, a.n_heads), kThreads, 0, st>>>(a);
 }
 
 void launch_ssd_out(const PrefillArgs& a, hipStream_t st) {
-    ssd_out_kernel<<<dim3(a.max_chunks, a.n_heads), 256, 0, st>>>(a);
+    ssd_out_kernel<<<dim3(a.max_chunks, a.n_heads), kThreads, 0, st>>>(a);
 }
 
 }  // namespace nhm
