@@ -15,11 +15,12 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // float -> bfloat16 bits, round half to even; NaN becomes a quiet NaN with its sign.
+// Both results are computed and one is selected, so the conversion never diverges.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? nan : r;
 }
 
 // float -> OCP FP8 E4M3FN code: round half to even, saturating at +-448 (infinities
@@ -31,16 +32,12 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
     const uint32_t u = __float_as_uint(v);
     const uint32_t s = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7fffffffu;
-    uint32_t c;
-    if (a > 0x7f800000u) {
-        c = 0x7fu;
-    } else if (a >= 0x43e00000u) {          // 448.0f
-        c = 0x7eu;
-    } else if (a < 0x3c800000u) {           // 2^-6
-        c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    } else {
-        c = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    }
+    // every branch is evaluated and selected (no divergence); the subnormal one on a clamped input
+    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a < 0x3c800000u ? a : 0x3c800000u) * 512.0f);
+    const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t c = a < 0x3c800000u ? sub : nrm;   // 2^-6
+    c = a >= 0x43e00000u ? 0x7eu : c;           // 448.0f and above, infinities
+    c = a > 0x7f800000u ? 0x7fu : c;            // NaN
     return s | c;
 }
 

@@ -66,8 +66,11 @@ def test_linear_sweep_shapes(nhm, m, n, k):
     _check(nhm, a, w, ws, sa)
 
 
+# m <= 16: GEMV; m <= 640: panel kernel (128 x 192 tiles when they give >= 160 workgroups,
+# else 64 x 128); larger m: tile kernel. The ragged shapes cut every kind of tile edge.
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
-                                   (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688)])
+                                   (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
+                                   (500, 10000, 2672), (641, 130, 256), (700, 520, 272)])
 def test_linear_ragged(nhm, m, n, k):
     from workloads import linear_case
     a, w, ws, sa = linear_case(m, n, k, extra=7)
@@ -81,14 +84,22 @@ def test_linear_prequantized_input(nhm, m):
     _check(nhm, a, w, ws, sa, via_e4m3=True)
 
 
-@pytest.mark.parametrize("m", [2, 100])
-def test_linear_strided_output(nhm, m):
+# ld_pad 13 makes the row stride odd: the kernels fall back from 8-byte stores
+@pytest.mark.parametrize("m", [2, 100, 700])
+@pytest.mark.parametrize("ld_pad", [12, 13])
+def test_linear_strided_output(nhm, m, ld_pad):
     from workloads import linear_case
     a, w, ws, sa = linear_case(m, 520, 512, extra=4)
-    _check(nhm, a, w, ws, sa, ld_pad=12)
+    _check(nhm, a, w, ws, sa, ld_pad=ld_pad)
 
 
-@pytest.mark.parametrize("m", [8, 512])
+def test_linear_large_m(nhm):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(1024, 2688, 4096, extra=5)
+    _check(nhm, a, w, ws, sa)
+
+
+@pytest.mark.parametrize("m", [8, 200, 512, 700])
 def test_linear_deterministic(nhm, m):
     from tests.gpu_util import dev, host
     from workloads import linear_case
