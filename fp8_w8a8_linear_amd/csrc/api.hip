@@ -129,13 +129,15 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     return w;
 }
 
-// The weight-streaming GEMV serves m <= 16 (and k up to 16384); the tiled GEMM the rest.
-static bool use_gemv(int64_t m, int64_t k) { return m <= 16 && k <= 16384; }
+// The weight-streaming GEMV serves m <= 16 (k up to 16384, weights under 2 GiB: its buffer
+// descriptors take 32-bit offsets); the tiled GEMM the rest. A decode step always takes
+// the GEMV, which carries the conv epilogue, and reports geometries beyond its limits.
+static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
 
 // One projection on an e4m3 activation [m, lda].
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
                           int64_t ld_out, const ConvEpilogue* conv, hipStream_t st) {
-    if (use_gemv(m, w.k))
+    if (conv || use_gemv(m, w.n, w.k))
         return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st);
     return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
 }

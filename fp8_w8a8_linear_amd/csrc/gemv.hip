@@ -18,28 +18,6 @@ namespace nhm {
 
 constexpr int kGemvMaxSteps = 8;       // k-steps per wave held in registers
 
-// 32 bytes of row `row` starting at byte `kb`, zero beyond k or for rows >= nrows.
-// Weight rows are streamed once: non-temporal loads keep them out of the caches.
-template <bool kStream>
-__device__ __forceinline__ v8i load32(const uint8_t* base, int64_t ld, int64_t row, int64_t nrows, int64_t kb,
-                                      int64_t k) {
-    v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row < nrows) {
-        const uint8_t* p = base + row * ld + kb;
-        if (kb + 16 <= k) {
-            const v4u lo = kStream ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p))
-                                   : *reinterpret_cast<const v4u*>(p);
-            v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-        }
-        if (kb + 32 <= k) {
-            const v4u hi = kStream ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 16))
-                                   : *reinterpret_cast<const v4u*>(p + 16);
-            v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-        }
-    }
-    return v;
-}
-
 struct GemvArgs {
     const uint8_t* a; int64_t lda; int m;
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
@@ -48,6 +26,21 @@ struct GemvArgs {
     ConvEpilogue conv;
 };
 
+// 32 bytes of an operand row through a buffer descriptor: the descriptor's range check
+// returns zeros for offsets past the operand, so rows >= nrows and k beyond the end
+// need no branches (the caller passes kGemvOut for them).
+constexpr uint32_t kGemvOut = 0x80000000u;
+template <int kAux>
+__device__ __forceinline__ v8i bload32(const __amdgpu_buffer_rsrc_t& r, uint32_t lo_off, uint32_t hi_off) {
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(r, lo_off, 0, kAux);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(r, hi_off, 0, kAux);
+    v8i v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return v;
+}
+constexpr int kStreamAux = 2;   // non-temporal: weight rows are read exactly once
+
 template <int kWaves, bool kConv>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves][64];
@@ -55,19 +48,65 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t row = n0 + (lane & 15);       // A operand row (feature)
     const int col = lane & 15;                  // B operand column (token)
-    const int64_t kq = (lane >> 4) * 32;
+    const int kq = (lane >> 4) * 32;
+
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
+    const uint32_t wrow = row < g.n ? (uint32_t)(row * g.k) : kGemvOut;
+    const uint32_t arow = col < g.m ? (uint32_t)(col * g.lda) : kGemvOut;
 
     v8i wa[kGemvMaxSteps], xb[kGemvMaxSteps];
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i) {
         const int s = wave + i * kWaves;
-        if (s < g.ksteps) wa[i] = load32<true>(g.w, g.k, row, g.n, (int64_t)s * 128 + kq, g.k);
+        if (s < g.ksteps) {                     // wave-uniform
+            const int kb = s * 128 + kq;
+            wa[i] = bload32<kStreamAux>(wrs, kb < g.k ? wrow + kb : kGemvOut, kb + 16 < g.k ? wrow + kb + 16 : kGemvOut);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i) {
         const int s = wave + i * kWaves;
-        if (s < g.ksteps) xb[i] = load32<false>(g.a, g.lda, col, g.m, (int64_t)s * 128 + kq, g.k);
+        if (s < g.ksteps) {
+            const int kb = s * 128 + kq;
+            xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
+        }
     }
+
+    // wave 0 stores the result: fetch what its epilogue reads while the weights stream in
+    const int64_t nbase = n0 + 4 * (lane >> 4);
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    uint2 w0{}, w1{}, w2{}, cb{};
+    uint4 cw0{}, cw1{};
+    int slot = -1;
+    int64_t ch = -1;
+    if (wave == 0) {
+        const float sa = *g.a_scale;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t nn = nbase + r;
+            sc[r] = sa * g.w_scale[nn < g.n ? nn : g.n - 1];
+        }
+        if constexpr (kConv) {
+            const ConvEpilogue& c = g.conv;
+            ch = nbase - c.xbc_off;
+            if (ch >= 0 && ch < c.conv_dim && col < g.m) {
+                slot = c.slot_idx[col];
+                cw0 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4);      // taps of channels ch, ch+1
+                cw1 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4 + 8);  // channels ch+2, ch+3
+                cb = *reinterpret_cast<const uint2*>(c.conv_b + ch);
+                if (slot >= 0) {
+                    const uint16_t* win = c.conv_pool + (int64_t)slot * 3 * c.conv_dim + ch;
+                    w0 = *reinterpret_cast<const uint2*>(win);
+                    w1 = *reinterpret_cast<const uint2*>(win + c.conv_dim);
+                    w2 = *reinterpret_cast<const uint2*>(win + 2 * c.conv_dim);
+                }
+            } else {
+                ch = -1;
+            }
+        }
+    }
+
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i)
@@ -81,14 +120,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
     // acc[r] = D[feature nbase + r][token col]
     if (col >= g.m) return;
-    const int64_t nbase = n0 + 4 * (lane >> 4);
-    const float sa = *g.a_scale;
     uint32_t hb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t nn = nbase + r;
-        hb[r] = f32_to_bf16(nn < g.n ? acc[r] * sa * g.w_scale[nn] : 0.f);
-    }
+    for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[r] * sc[r]);
     uint16_t* o = g.out + (int64_t)col * g.ld_out + nbase;
     if (g.vec_out && nbase + 3 < g.n) {
         *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
@@ -100,21 +134,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     if constexpr (kConv) {
         // causal depthwise conv (width 4) + SiLU on the xBC features, window shift in place
         const ConvEpilogue& c = g.conv;
-        const int64_t ch = nbase - c.xbc_off;
-        if (ch < 0 || ch >= c.conv_dim) return;
-        const int slot = c.slot_idx[col];
+        if (ch < 0) return;
         uint16_t* xo = c.xbc_conv + (int64_t)col * c.conv_dim + ch;
         if (slot < 0) {
             *reinterpret_cast<uint2*>(xo) = make_uint2(0u, 0u);
             return;
         }
         uint16_t* win = c.conv_pool + (int64_t)slot * 3 * c.conv_dim + ch;
-        const uint2 w0 = *reinterpret_cast<const uint2*>(win);
-        const uint2 w1 = *reinterpret_cast<const uint2*>(win + c.conv_dim);
-        const uint2 w2 = *reinterpret_cast<const uint2*>(win + 2 * c.conv_dim);
-        const uint4 cw0 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4);      // channels ch, ch+1
-        const uint4 cw1 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4 + 8);  // channels ch+2, ch+3
-        const uint2 cb = *reinterpret_cast<const uint2*>(c.conv_b + ch);
         const uint32_t u0[4] = {w0.x & 0xffffu, w0.x >> 16, w0.y & 0xffffu, w0.y >> 16};
         const uint32_t u1[4] = {w1.x & 0xffffu, w1.x >> 16, w1.y & 0xffffu, w1.y >> 16};
         const uint32_t u2[4] = {w2.x & 0xffffu, w2.x >> 16, w2.y & 0xffffu, w2.y >> 16};
@@ -150,6 +176,8 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     g.conv = conv ? *conv : ConvEpilogue{};
     if (g.ksteps > 16 * kGemvMaxSteps)
         return fail(NHM_ERR_UNSUPPORTED, "gemv: k %lld exceeds %d", (long long)k, 16 * 128 * kGemvMaxSteps);
+    if (n * k >= (int64_t(1) << 31) || (int64_t)m * lda >= (int64_t(1) << 31))
+        return fail(NHM_ERR_UNSUPPORTED, "gemv: operands of 2 GiB or more");
     // 4 waves up to 23 k-steps (k < 2944), then 8, then 16
     const int waves = g.ksteps < 24 ? 4 : (g.ksteps <= 8 * kGemvMaxSteps ? 8 : 16);
     const dim3 grid((unsigned)((n + 15) / 16));
