@@ -2,7 +2,7 @@
 """Mixer throughput on one MI355X: paged decode B=8 through 23 stacked blocks (the
 headline line) and prefill of one 512-token sequence through one block.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
 
 A step is one decode token for each of 8 sequences through all 23 mixer blocks
 (nhm_mixer_decode per block, state rows updated in place), replayed as one HIP
@@ -44,6 +44,24 @@ def decode_bytes_per_layer(B):
     return w + scales + small + B * per_seq
 
 
+# HBM bytes one launch of the roofline kernel actually moved, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, per dispatch) of `bench.py --copy-probe`, each scaled by what
+# the same counter reads for the 256 MiB device copy of that run. Valid only for the kernel
+# sources it was measured on: reported as null once their hash differs.
+TRAFFIC = {"sources": ["fp8_w8a8_linear_amd/csrc/gemv.hip", "fp8_w8a8_linear_amd/csrc/nhm_device.h"],
+           "sha256": "63d627da7fbd33eebc70b639a01651e741ce1a0c523403cfa49368aff86651b1",
+           "bytes_per_launch": 28190969}
+
+
+def measured_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return TRAFFIC["bytes_per_launch"] if h.hexdigest() == TRAFFIC["sha256"] else None
+
+
 def gemv_bytes(m, n, k):
     """Algorithmic bytes of one W8A8 GEMV: weight + per-channel scales + e4m3 input + bf16 output."""
     return n * k + 4 * n + m * k + 2 * m * n
@@ -55,6 +73,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle parity sample and cpu_baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a 256 MiB device-to-device copy and negation (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the mixer shards by sequence with no "
@@ -71,6 +91,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        src = torch.randn(64 << 20, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x (copy_ + neg) of 256 MiB float32 done")
+        del src, dst
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -264,7 +294,7 @@ def main():
                             "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel (in_proj 10304x2688, m=8)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "us_per_launch": round(gemv_us, 3), "bytes_per_launch": gb},
         "prefill_512": {"tokens_per_s": round(T / (pre_us * 1e-6), 1), "us_per_block": round(pre_us, 1),
                         "gemm": gemm, "gemm_bound": "mfma", "gemm_tflops": round(gemm_tflops, 1),
