@@ -367,6 +367,13 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
         if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, st)) != NHM_OK) return s;
+        // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every
+        // later token's decay exponentiates: its columns are recomputed with exact f32
+        // accumulation (the GEMV that serves small m accumulates exactly already)
+        if (!use_gemv(n_tokens, p->in_proj.n, p->in_proj.k) &&
+            (s = launch_exact_columns(q_in, H, n_tokens, p->in_proj.w, p->in_proj.w_scale, p->in_proj.a_scale,
+                                      p->in_proj.n, p->in_proj.k, l.dt_off, p->g.n_heads, zx, l.d_in_proj, st)) != NHM_OK)
+            return s;
     }
     PrefillArgs a;
     a.T = n_tokens;

@@ -1,9 +1,10 @@
 // Weight-streaming FP8 W8A8 GEMV for m <= 16 rows (decode).
 //
 // The problem is HBM-bound: every weight byte is read exactly once and the
-// activations (m x k e4m3, a few KB) stay in L2/L1. The contraction still runs on
-// the 16x16x128 e4m3 MFMA: 16 weight rows are the A operand, the (zero-padded) 16
-// activation rows the B operand, so the VALU never converts fp8.
+// activations (m x k e4m3, a few KB) stay in L2/L1. The contraction runs on the MFMA
+// with 16 weight rows as the A operand and the (zero-padded) 16 activation rows as
+// the B operand; the e4m3 codes are converted to bf16 in registers (exact) and summed
+// by the bf16 MFMA, which accumulates in full f32.
 //
 // Decomposition: one workgroup owns 16 output features and the whole k range; its
 // waves take the 128-wide k-steps round-robin (neighbouring waves read neighbouring
@@ -55,6 +56,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     const uint32_t wrow = row < g.n ? (uint32_t)(row * g.k) : kGemvOut;
     const uint32_t arow = col < g.m ? (uint32_t)(col * g.lda) : kGemvOut;
 
+    // weight and activation pieces of each k-step are issued together, so a step's
+    // MFMAs wait only for the loads before them
     v8i wa[kGemvMaxSteps], xb[kGemvMaxSteps];
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i) {
@@ -62,13 +65,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         if (s < g.ksteps) {                     // wave-uniform
             const int kb = s * 128 + kq;
             wa[i] = bload32<kStreamAux>(wrs, kb < g.k ? wrow + kb : kGemvOut, kb + 16 < g.k ? wrow + kb + 16 : kGemvOut);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kGemvMaxSteps; ++i) {
-        const int s = wave + i * kWaves;
-        if (s < g.ksteps) {
-            const int kb = s * 128 + kq;
             xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
         }
     }
@@ -107,10 +103,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         }
     }
 
+    // Exact f32 accumulation: each 128-k step runs as four bf16 MFMAs on the converted codes
+    // (sub-step j takes bytes 8j .. 8j+7 of the lane's 32, the same bytes of both operands).
+    // The e4m3 MFMA would be 4x fewer instructions but sums coarser than f32; this kernel is
+    // bound by the weight stream, and the conversions and MFMAs hide under it.
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kGemvMaxSteps; ++i)
-        if (wave + i * kWaves < g.ksteps) acc = mfma_e4m3(wa[i], xb[i], acc);
+        if (wave + i * kWaves < g.ksteps) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * j], wa[i][2 * j + 1]),
+                                e4m3x8_to_bf16(xb[i][2 * j], xb[i][2 * j + 1]), acc);
+        }
 
     if (wave > 0) s_red[wave][lane] = acc;
     __syncthreads();
@@ -162,6 +167,81 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         *reinterpret_cast<uint2*>(win + c.conv_dim) = w2;
         *reinterpret_cast<uint2*>(win + 2 * c.conv_dim) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
     }
+}
+
+// ---------------------------------------------------------------- exact columns
+// Recomputes output columns [c0, c0 + nc) of a W8A8 projection with exact f32
+// accumulation (bf16 MFMA on the converted codes), over all m rows. The mixer uses
+// it for the 64 dt columns of in_proj after the e4m3 GEMM: dt enters the scan through
+// exp(dt * A) of every later token, where one bf16 step of dt_raw moves a long-memory
+// head's state by up to a percent, so dt gets the accumulation the reference
+// prescribes rather than the e4m3 MFMA's coarser sum. A workgroup owns one 16 x 16
+// tile (16 rows, 16 columns); its 8 waves take the k-steps round robin with all their
+// loads in flight at once, and the partial tiles are summed through LDS in wave order,
+// as in the GEMV.
+constexpr int kExactWaves = 8, kExactSteps = 4;   // k-steps per wave per pass
+__global__ __launch_bounds__(kExactWaves * 64) void exact_columns_kernel(const GemvArgs g, int64_t c0, int64_t nc) {
+    __shared__ v4f s_red[kExactWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 16 + (lane & 15);                  // B operand row (token)
+    const int64_t cb = c0 + (int64_t)blockIdx.y * 16;
+    const int kq = (lane >> 4) * 32;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
+    const uint32_t arow = t < g.m ? (uint32_t)(t * g.lda) : kGemvOut;
+    const int64_t cw = cb + (lane & 15);                                          // A operand row (column)
+    const uint32_t wrow = cw < c0 + nc ? (uint32_t)(cw * g.k) : kGemvOut;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wave; s0 < g.ksteps; s0 += kExactWaves * kExactSteps) {   // one pass for k <= 4096
+        v8i xb[kExactSteps], wa[kExactSteps];
+#pragma unroll
+        for (int i = 0; i < kExactSteps; ++i) {
+            const int s = s0 + i * kExactWaves;
+            const int kb = s * 128 + kq;
+            const bool in = s < g.ksteps && kb < g.k, in2 = s < g.ksteps && kb + 16 < g.k;
+            xb[i] = bload32<0>(ars, in ? arow + kb : kGemvOut, in2 ? arow + kb + 16 : kGemvOut);
+            wa[i] = bload32<0>(wrs, in ? wrow + kb : kGemvOut, in2 ? wrow + kb + 16 : kGemvOut);
+        }
+#pragma unroll
+        for (int i = 0; i < kExactSteps; ++i) {
+            if (s0 + i * kExactWaves >= g.ksteps) break;                      // wave-uniform
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub)
+                acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * sub], wa[i][2 * sub + 1]),
+                                e4m3x8_to_bf16(xb[i][2 * sub], xb[i][2 * sub + 1]), acc);
+        }
+    }
+    if (wave > 0) s_red[wave][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < kExactWaves; ++w) acc += s_red[w][lane];
+    // acc[r] = D[column cb + 4 (lane / 16) + r][token t]
+    if (t >= g.m) return;
+    const float sa = *g.a_scale;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t c = cb + 4 * (lane >> 4) + r;
+        if (c < c0 + nc) g.out[t * g.ld_out + c] = (uint16_t)f32_to_bf16(acc[r] * (sa * g.w_scale[c]));
+    }
+}
+
+nhm_status launch_exact_columns(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
+                                const float* a_scale, int64_t n, int64_t k, int64_t c0, int64_t nc, uint16_t* out,
+                                int64_t ld_out, hipStream_t st) {
+    if (m == 0 || nc == 0) return NHM_OK;
+    if (c0 < 0 || nc < 0 || c0 + nc > n) return fail(NHM_ERR_SHAPE, "exact columns [%lld, %lld) outside [0, %lld)",
+                                                     (long long)c0, (long long)(c0 + nc), (long long)n);
+    if (n * k >= (int64_t(1) << 31) || m * lda >= (int64_t(1) << 31))
+        return fail(NHM_ERR_UNSUPPORTED, "exact columns: operands of 2 GiB or more");
+    GemvArgs g{};
+    g.a = a; g.lda = lda; g.m = (int)m;
+    g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
+    g.out = out; g.ld_out = ld_out;
+    g.ksteps = (int)((k + 127) / 128);
+    const dim3 grid((unsigned)((m + 15) / 16), (unsigned)((nc + 15) / 16));
+    exact_columns_kernel<<<grid, dim3(kExactWaves * 64), 0, st>>>(g, c0, nc);
+    return check_launch("exact columns");
 }
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,

@@ -80,5 +80,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ v4f mfma_e4m3(const v8i& a, const v8i& b, const v4f& c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// The e4m3 MFMA sums its 128 products in a narrower adder than f32: measured on MI355X,
+// up to ~2^-17 of sum |a b| per instruction (and 32x32x64 the same). Where exact f32
+// accumulation is wanted, the codes go through the bf16 MFMA instead: every e4m3 value
+// is exact in bf16, and the bf16 16x16x32 MFMA sums its 32 exact products to within
+// ~0.2 * 2^-24 of sum |a b| (measured).
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 16x16x32 bf16 MFMA, f32 accumulate: lane l supplies row (l % 16) of A and column
+// (l % 16) of B, 8 consecutive k of the 32-k step chosen by l / 16.
+__device__ __forceinline__ v4f mfma_bf16(const bf16x8& a, const bf16x8& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight e4m3 codes (two dwords, memory order) as exact bf16 values (hardware convert, scale 1).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    // whole-register bit casts (no element extraction): each pair is one dword, low half first
+    const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+    return __builtin_bit_cast(bf16x8, u);
+}
 
 }  // namespace nhm

@@ -43,6 +43,11 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        const ConvEpilogue* conv, hipStream_t st);
 
+// Recomputes columns [c0, c0 + nc) of out = W8A8(a, w) with exact f32 accumulation (gemv.hip).
+nhm_status launch_exact_columns(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
+                                const float* a_scale, int64_t n, int64_t k, int64_t c0, int64_t nc, uint16_t* out,
+                                int64_t ld_out, hipStream_t st);
+
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,

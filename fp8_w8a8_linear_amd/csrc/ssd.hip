@@ -23,17 +23,11 @@
 
 namespace nhm {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kHP = 64;    // head_dim
 constexpr int kDS = 128;   // d_state
 constexpr int kQ = 128;    // chunk length
 constexpr int kLd = 136;   // LDS row stride in bf16 (272 bytes: 16-byte aligned rows)
 constexpr int kThreads = 512;
-
-__device__ __forceinline__ v4f mfma_bf16(const bf16x8& a, const bf16x8& b, const v4f& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 

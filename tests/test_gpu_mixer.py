@@ -267,3 +267,88 @@ def test_prefill_carry_split(nhm, block0):
     assert rel_max(bf16_to_f64(np.concatenate([o1, o2])), bf16_to_f64(ow)) <= TOL_OUT
     assert rel_l2(sp2[0], spw[0]) <= TOL_STATE
     assert np.array_equal(cp2[0], cpw[0])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_prefill_ragged_15360_23_blocks(nhm):
+    """Ragged prefill of 4 sequences (8192, 4096, 2048, 1024 tokens, zero initial state)
+    through 23 stacked blocks, each block's output the next one's input.
+
+    Layer 0 is checked in full against the oracle (every token, every final state and
+    window). Layers 11 and 22 are checked on the shortest sequence, with the oracle fed
+    the GPU's own input to that layer, so each check covers one block (the tolerance is
+    per block; the oracle and the GPU path would otherwise drift apart through 22 stacked
+    blocks of bf16/e4m3 rounding).
+    """
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from tests.gpu_util import dev, host, upload_params, ws_region, zeros_ws
+    from tests.oracle_workers import prefill_sequence
+    from workloads import RAGGED_LENGTHS, block_params, hidden, slots
+    W, S, L = 4, 8, 23
+    lens = list(RAGGED_LENGTHS)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    assert T == 15360 and len(lens) == 4
+    sl = slots(W, len(lens), S)
+    short = int(np.argmin(lens))
+    rows_short = list(range(int(cu[short]), int(cu[short + 1])))
+    x = hidden(W, T)
+    lay = nhm.prefill_ws_layout(T, len(lens))
+    ws = zeros_ws(lay["total"])
+    cud, sld, hid = dev(cu), dev(sl), dev(np.zeros(len(lens), np.int32))
+    check = {0: list(range(len(lens))), 11: [short], 22: [short]}
+    got = {}
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=6, mp_context=ctx) as pool:
+        jobs = {}
+        xd = dev(x)
+        for layer in range(L):
+            if layer in check:
+                xh = host(xd)
+                for i in check[layer]:
+                    jobs[(layer, i)] = pool.submit(prefill_sequence, (W, layer, xh[cu[i]:cu[i + 1]]))
+            pd = upload_params(block_params(W, layer))
+            spd = torch.zeros((S, 64, 64, 128), dtype=torch.float32, device="cuda")
+            cpd = torch.zeros((S, 3, 6144), dtype=torch.int16, device="cuda")
+            out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+            nhm.mixer_prefill(pd, xd, cud, sld, hid, spd, cpd, out, ws)
+            torch.cuda.synchronize()
+            if layer in check:
+                got[layer] = dict(out=host(out), sp=host(spd), cp=host(cpd),
+                                  q=ws_region(ws, lay["q_out"], T * I, np.uint8).reshape(T, I),
+                                  norm=ws_region(ws, lay["norm"], T * I, np.uint16).reshape(T, I),
+                                  q_in=ws_region(ws, lay["q_in"], T * H, np.uint8).reshape(T, H))
+            xd = out
+        refs = {key: f.result() for key, f in jobs.items()}
+
+    from tests.gpu_util import block_parity, rel_l2, rel_max
+    from oracle import bf16_to_f64
+    failures = []
+    for layer, seqs in check.items():
+        g = got[layer]
+        p = block_params(W, layer)
+        rows = [r for i in seqs for r in range(int(cu[i]), int(cu[i + 1]))]
+        ref_out = np.concatenate([refs[(layer, i)]["out"] for i in seqs])
+        ref_norm = np.concatenate([refs[(layer, i)]["norm"] for i in seqs])
+        ref_q = np.concatenate([refs[(layer, i)]["q_out"] for i in seqs])
+        if layer == 0:
+            ref_qin = np.concatenate([refs[(layer, i)]["q_in"] for i in seqs])
+            assert np.array_equal(g["q_in"], ref_qin)                                        # a1, every token
+        try:
+            m = block_parity(g["out"][rows], g["q"][rows], g["norm"][rows], ref_out, ref_norm, ref_q, p)
+        except AssertionError as e:
+            m = f"FAILED: {e}"
+            failures.append(f"layer {layer}: {e}")
+        states = []
+        for i in seqs:
+            r = rel_l2(g["sp"][sl[i]], refs[(layer, i)]["state"])
+            states.append(round(float(r), 7))
+            if r > TOL_STATE:
+                failures.append(f"layer {layer} sequence {i}: state rel l2 {r:.3g}")
+            a, b = bf16_to_f64(g["cp"][sl[i]]), bf16_to_f64(refs[(layer, i)]["window"])
+            if not (rel_l2(a, b) <= TOL_STATE and rel_max(a, b) <= TOL_OUT):
+                failures.append(f"layer {layer} sequence {i} window")
+        print(f"layer {layer} sequences {seqs} (rows {rows[0]}..{rows[-1]}): {m}, state rel l2 {states}")
+    assert not failures, "; ".join(failures)
