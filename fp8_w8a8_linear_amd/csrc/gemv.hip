@@ -42,7 +42,7 @@ __device__ __forceinline__ v8i bload32(const __amdgpu_buffer_rsrc_t& r, uint32_t
 }
 constexpr int kStreamAux = 2;   // non-temporal: weight rows are read exactly once
 
-template <int kWaves, bool kConv>
+template <int kWaves, int kSteps, bool kConv>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -50,72 +50,70 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     const int64_t row = n0 + (lane & 15);       // A operand row (feature)
     const int col = lane & 15;                  // B operand column (token)
     const int kq = (lane >> 4) * 32;
+    const int64_t nbase = n0 + 4 * (lane >> 4);
+
+    // Everything up to the MFMAs is straight-line code: loads past the operands go to an
+    // out-of-range buffer offset (zeros) and indexes are clamped, so the compiler can wait
+    // for each k-step's loads alone instead of for all outstanding loads at a branch join.
+    // First the small operands of the epilogue (so that waiting for them later does not
+    // wait for the weight stream), then the weight stream, k-step by k-step.
+    const float sa = *g.a_scale;
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nbase + r < g.n ? nbase + r : g.n - 1];
+    int slot = -1;
+    int64_t ch = -1;
+    uint4 cw0{}, cw1{};
+    uint2 cb{};
+    if constexpr (kConv) {
+        const ConvEpilogue& c = g.conv;
+        ch = nbase - c.xbc_off;
+        const int64_t chc = ch < 0 ? 0 : (ch > c.conv_dim - 4 ? c.conv_dim - 4 : ch);
+        slot = c.slot_idx[col < g.m ? col : 0];
+        cw0 = *reinterpret_cast<const uint4*>(c.conv_w + chc * 4);      // taps of channels ch, ch+1
+        cw1 = *reinterpret_cast<const uint4*>(c.conv_w + chc * 4 + 8);  // channels ch+2, ch+3
+        cb = *reinterpret_cast<const uint2*>(c.conv_b + chc);
+        if (ch >= c.conv_dim || col >= g.m) ch = -1;
+    }
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
     const uint32_t wrow = row < g.n ? (uint32_t)(row * g.k) : kGemvOut;
     const uint32_t arow = col < g.m ? (uint32_t)(col * g.lda) : kGemvOut;
-
-    // weight and activation pieces of each k-step are issued together, so a step's
-    // MFMAs wait only for the loads before them
-    v8i wa[kGemvMaxSteps], xb[kGemvMaxSteps];
+    // weight and activation pieces of each k-step are issued together
+    v8i wa[kSteps], xb[kSteps];
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSteps; ++i) {
-        const int s = wave + i * kWaves;
-        if (s < g.ksteps) {                     // wave-uniform
-            const int kb = s * 128 + kq;
-            wa[i] = bload32<kStreamAux>(wrs, kb < g.k ? wrow + kb : kGemvOut, kb + 16 < g.k ? wrow + kb + 16 : kGemvOut);
-            xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
-        }
+    for (int i = 0; i < kSteps; ++i) {
+        const int kb = (wave + i * kWaves) * 128 + kq;
+        wa[i] = bload32<kStreamAux>(wrs, kb < g.k ? wrow + kb : kGemvOut, kb + 16 < g.k ? wrow + kb + 16 : kGemvOut);
+        xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
     }
-
-    // wave 0 stores the result: fetch what its epilogue reads while the weights stream in
-    const int64_t nbase = n0 + 4 * (lane >> 4);
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
-    uint2 w0{}, w1{}, w2{}, cb{};
-    uint4 cw0{}, cw1{};
-    int slot = -1;
-    int64_t ch = -1;
-    if (wave == 0) {
-        const float sa = *g.a_scale;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t nn = nbase + r;
-            sc[r] = sa * g.w_scale[nn < g.n ? nn : g.n - 1];
-        }
-        if constexpr (kConv) {
-            const ConvEpilogue& c = g.conv;
-            ch = nbase - c.xbc_off;
-            if (ch >= 0 && ch < c.conv_dim && col < g.m) {
-                slot = c.slot_idx[col];
-                cw0 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4);      // taps of channels ch, ch+1
-                cw1 = *reinterpret_cast<const uint4*>(c.conv_w + ch * 4 + 8);  // channels ch+2, ch+3
-                cb = *reinterpret_cast<const uint2*>(c.conv_b + ch);
-                if (slot >= 0) {
-                    const uint16_t* win = c.conv_pool + (int64_t)slot * 3 * c.conv_dim + ch;
-                    w0 = *reinterpret_cast<const uint2*>(win);
-                    w1 = *reinterpret_cast<const uint2*>(win + c.conv_dim);
-                    w2 = *reinterpret_cast<const uint2*>(win + 2 * c.conv_dim);
-                }
-            } else {
-                ch = -1;
-            }
-        }
+    // the carried conv window of this token's sequence (slot row 0 stands in for a padded row)
+    uint2 w0{}, w1{}, w2{};
+    if constexpr (kConv) {
+        const ConvEpilogue& c = g.conv;
+        const int64_t chc = ch < 0 ? 0 : ch;
+        const uint16_t* win = c.conv_pool + (int64_t)(slot < 0 ? 0 : slot) * 3 * c.conv_dim + chc;
+        w0 = *reinterpret_cast<const uint2*>(win);
+        w1 = *reinterpret_cast<const uint2*>(win + c.conv_dim);
+        w2 = *reinterpret_cast<const uint2*>(win + 2 * c.conv_dim);
     }
+    // keep every load above issued before the first MFMA (the scheduler would otherwise sink
+    // later steps' loads below earlier steps' MFMAs, serialising the stream)
+    __builtin_amdgcn_sched_barrier(0);
 
     // Exact f32 accumulation: each 128-k step runs as four bf16 MFMAs on the converted codes
     // (sub-step j takes bytes 8j .. 8j+7 of the lane's 32, the same bytes of both operands).
     // The e4m3 MFMA would be 4x fewer instructions but sums coarser than f32; this kernel is
-    // bound by the weight stream, and the conversions and MFMAs hide under it.
+    // bound by the weight stream, and the conversions and MFMAs of a step run while later
+    // steps are still streaming in. Steps past k hold zeros and add nothing.
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSteps; ++i)
-        if (wave + i * kWaves < g.ksteps) {
+    for (int i = 0; i < kSteps; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * j], wa[i][2 * j + 1]),
-                                e4m3x8_to_bf16(xb[i][2 * j], xb[i][2 * j + 1]), acc);
-        }
+        for (int j = 0; j < 4; ++j)
+            acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * j], wa[i][2 * j + 1]), e4m3x8_to_bf16(xb[i][2 * j], xb[i][2 * j + 1]),
+                            acc);
 
     if (wave > 0) s_red[wave][lane] = acc;
     __syncthreads();
@@ -258,17 +256,28 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
         return fail(NHM_ERR_UNSUPPORTED, "gemv: k %lld exceeds %d", (long long)k, 16 * 128 * kGemvMaxSteps);
     if (n * k >= (int64_t(1) << 31) || (int64_t)m * lda >= (int64_t(1) << 31))
         return fail(NHM_ERR_UNSUPPORTED, "gemv: operands of 2 GiB or more");
-    // 4 waves up to 23 k-steps (k < 2944), then 8, then 16
+    // 4 waves up to 23 k-steps (k < 2944), then 8, then 16; each wave holds its steps in
+    // registers, their count rounded up to 2, 4, 6 or 8
     const int waves = g.ksteps < 24 ? 4 : (g.ksteps <= 8 * kGemvMaxSteps ? 8 : 16);
+    const int per = (g.ksteps + waves - 1) / waves;
+    const int steps = per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
     const dim3 grid((unsigned)((n + 15) / 16));
-#define NHM_GEMV_LAUNCH(W)                                                  \
-    do {                                                                    \
-        if (conv) gemv_kernel<W, true><<<grid, dim3(W * 64), 0, st>>>(g);  \
-        else gemv_kernel<W, false><<<grid, dim3(W * 64), 0, st>>>(g);      \
+#define NHM_GEMV_LAUNCH(W, S)                                                  \
+    do {                                                                       \
+        if (conv) gemv_kernel<W, S, true><<<grid, dim3(W * 64), 0, st>>>(g);  \
+        else gemv_kernel<W, S, false><<<grid, dim3(W * 64), 0, st>>>(g);      \
     } while (0)
-    if (waves == 4) NHM_GEMV_LAUNCH(4);
-    else if (waves == 8) NHM_GEMV_LAUNCH(8);
-    else NHM_GEMV_LAUNCH(16);
+#define NHM_GEMV_STEPS(W)                         \
+    do {                                          \
+        if (steps == 2) NHM_GEMV_LAUNCH(W, 2);    \
+        else if (steps == 4) NHM_GEMV_LAUNCH(W, 4); \
+        else if (steps == 6) NHM_GEMV_LAUNCH(W, 6); \
+        else NHM_GEMV_LAUNCH(W, 8);               \
+    } while (0)
+    if (waves == 4) NHM_GEMV_STEPS(4);
+    else if (waves == 8) NHM_GEMV_STEPS(8);
+    else NHM_GEMV_STEPS(16);
+#undef NHM_GEMV_STEPS
 #undef NHM_GEMV_LAUNCH
     return check_launch("gemv");
 }
