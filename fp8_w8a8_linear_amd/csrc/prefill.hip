@@ -153,10 +153,9 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a) {
 
 // New window of sequence i: the last three rows of [initial window; its tokens].
 // Runs after conv_fwd_kernel has read every initial window.
-__global__ __launch_bounds__(256) void conv_store_kernel(const PrefillArgs a) {
-    const int c8 = blockIdx.x * 256 + threadIdx.x;
-    const int i = blockIdx.y;
-    if (c8 * 8 >= a.conv_dim) return;
+// The carried window of sequence i after the call: the last 3 rows of [old window; tokens],
+// 8 channels (c8 .. c8+7) per call. Runs after every conv read of the old window.
+__device__ __forceinline__ void store_window(const PrefillArgs& a, int i, int c8) {
     const int64_t s0 = a.cu_seqlens[i];
     const int64_t L = a.cu_seqlens[i + 1] - s0;
     uint4 v[3];
@@ -171,13 +170,17 @@ __global__ __launch_bounds__(256) void conv_store_kernel(const PrefillArgs a) {
     for (int r = 0; r < 3; ++r) dst[(int64_t)r * a.conv_dim / 8] = v[r];
 }
 
-// ---------------------------------------------------------------- SSD: state passing
-
 // One workgroup per (sequence, head, block of 8 state rows). Walks the sequence's
 // chunks in order, replacing each S_c by the state entering chunk c, and leaves the
 // final state in the pool row (read first, written last by this workgroup only).
+// The first workgroups of each sequence also store its carried conv window (the conv
+// kernel, which reads the old window, has finished by now).
 __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
     const int i = blockIdx.x, h = blockIdx.y, pb = blockIdx.z, t = threadIdx.x;
+    {
+        const int c8 = (h * (kHP / 8) + pb) * 256 + t;      // 8-channel group of the window
+        if (c8 * 8 < a.conv_dim) store_window(a, i, c8);
+    }
     const int c0 = min(a.seq_chunk0[i], a.max_chunks), c1 = min(a.seq_chunk0[i + 1], a.max_chunks);
     const int64_t off = (int64_t)pb * 8 * kDS + 4 * t;
     float4* pool = reinterpret_cast<float4*>(a.ssm_pool + ((int64_t)a.slot_idx[i] * a.n_heads + h) * kHP * kDS + off);
@@ -208,7 +211,6 @@ nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     const int c8_blocks = (a.conv_dim / 8 + 255) / 256;
     if (a.T > 0)
         conv_fwd_kernel<<<dim3(c8_blocks, (unsigned)((a.T + kConvRun - 1) / kConvRun)), 256, 0, st>>>(a);
-    if (a.n_seqs > 0) conv_store_kernel<<<dim3(c8_blocks, a.n_seqs), 256, 0, st>>>(a);
     if (a.max_chunks > 0) launch_ssd_state(a, st);
     if (a.n_seqs > 0) ssd_pass_kernel<<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
     if (a.max_chunks > 0) launch_ssd_out(a, st);
