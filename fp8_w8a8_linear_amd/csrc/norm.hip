@@ -10,6 +10,10 @@
 
 namespace nhm {
 
+// kIt > 0: groups of up to kIt * 512 channels; v = y * silu(z) is kept in registers
+// between the mean square and the output, so y and z are read once and the gate is
+// evaluated once per element. kIt == 0: any group width, two passes over y and z.
+template <int kIt>
 __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -19,29 +23,14 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     const int gw = a.d_inner / a.n_groups;
     const uint16_t* yr = a.y + tok * a.d_inner + (int64_t)g * gw;
     const uint16_t* zr = a.zxbcdt + tok * a.d_in_proj + a.z_off + (int64_t)g * gw;
-    float ss = 0.f;
-    for (int c = lane * 8; c < gw; c += 64 * 8) {
-        float y[8], z[8];
-        unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
-        unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float v = y[j] * silu(z[j]);
-            ss += v * v;
-        }
-    }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
     const float so = *a.out_a_scale;
-    for (int c = lane * 8; c < gw; c += 64 * 8) {
-        float y[8], z[8], w[8];
-        unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
-        unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
+    auto emit = [&](int c, const float (&v)[8], float r) {
+        float w[8];
         unpack8(*reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c), w);
         uint32_t ob[8], q[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            ob[j] = f32_to_bf16(y[j] * silu(z[j]) * r * w[j]);
+            ob[j] = f32_to_bf16(v[j] * r * w[j]);
             q[j >> 2] |= quant_bf16(ob[j], so) << (8 * (j & 3));
         }
         const int64_t o = tok * a.d_inner + (int64_t)g * gw + c;
@@ -49,12 +38,69 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
             *reinterpret_cast<uint4*>(a.norm + o) =
                 make_uint4(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16), ob[4] | (ob[5] << 16), ob[6] | (ob[7] << 16));
         *reinterpret_cast<uint2*>(a.q_out + o) = make_uint2(q[0], q[1]);
+    };
+    float ss = 0.f;
+    if constexpr (kIt > 0) {
+        float v[kIt][8];
+        uint4 yv[kIt], zv[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {                 // all loads first
+            const int c = lane * 8 + it * 512;
+            const int cc = c < gw ? c : 0;                 // in bounds; masked below
+            yv[it] = *reinterpret_cast<const uint4*>(yr + cc);
+            zv[it] = *reinterpret_cast<const uint4*>(zr + cc);
+        }
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            float y[8], z[8];
+            unpack8(yv[it], y);
+            unpack8(zv[it], z);
+            const bool in = lane * 8 + it * 512 < gw;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v[it][j] = in ? y[j] * silu(z[j]) : 0.f;
+                ss += v[it][j] * v[it][j];
+            }
+        }
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int c = lane * 8 + it * 512;
+            if (c < gw) emit(c, v[it], r);
+        }
+    } else {
+        for (int c = lane * 8; c < gw; c += 64 * 8) {
+            float y[8], z[8];
+            unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
+            unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = y[j] * silu(z[j]);
+                ss += v * v;
+            }
+        }
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
+        for (int c = lane * 8; c < gw; c += 64 * 8) {
+            float y[8], z[8], v[8];
+            unpack8(*reinterpret_cast<const uint4*>(yr + c), y);
+            unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = y[j] * silu(z[j]);
+            emit(c, v, r);
+        }
     }
 }
 
 nhm_status launch_gnorm_quant(const GnormArgs& a, hipStream_t st) {
     if (a.T <= 0) return NHM_OK;
-    gnorm_quant_kernel<<<dim3((unsigned)((a.T * a.n_groups + 3) / 4)), 256, 0, st>>>(a);
+    const dim3 grid((unsigned)((a.T * a.n_groups + 3) / 4));
+    const int gw = a.d_inner / a.n_groups;
+    if (gw <= 512) gnorm_quant_kernel<1><<<grid, 256, 0, st>>>(a);
+    else if (gw <= 1024) gnorm_quant_kernel<2><<<grid, 256, 0, st>>>(a);
+    else if (gw <= 2048) gnorm_quant_kernel<4><<<grid, 256, 0, st>>>(a);
+    else gnorm_quant_kernel<0><<<grid, 256, 0, st>>>(a);
     return check_launch("gnorm_quant");
 }
 
