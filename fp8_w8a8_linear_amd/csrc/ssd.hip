@@ -39,30 +39,34 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 
 __device__ __forceinline__ uint16_t bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
 
-// dt_s = softplus(dt_raw + bias) and the inclusive scan cs_s of dt_s * A over the
-// chunk (zero dt beyond L), in s_dt / s_cs; also stored for the other kernels.
-__device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, int64_t tok0, int L, float* s_dt,
+// dt_s = softplus(dt_raw + bias) (zero beyond L) and the inclusive scan cs_s of dt_s * A
+// over the chunk, in s_dt / s_cs, for the raw value u that thread s < Q loaded; also
+// stored for the other kernels. Threads 0..127 are waves 0 and 1: each scans its 64
+// values with lane shuffles, then wave 1 adds wave 0's total. Ends with a barrier.
+__device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, int L, float u, float* s_dt,
                                             float* s_cs) {
-    const int t = threadIdx.x;
-    const float A = -__expf(a.A_log[h]);
+    const int t = threadIdx.x, lane = t & 63;
+    __shared__ float s_w0;
+    float dt = 0.f, v = 0.f;
     if (t < kQ) {
-        float dt = 0.f;
-        if (t < L) dt = softplus(bf16_to_f32(a.zxbcdt[(tok0 + t) * a.d_in_proj + a.dt_off + h]) + a.dt_bias[h]);
-        s_dt[t] = dt;
-        s_cs[t] = dt * A;
+        dt = t < L ? softplus(u + a.dt_bias[h]) : 0.f;
+        v = dt * -__expf(a.A_log[h]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float w = __shfl_up(v, o, 64);
+            if (lane >= o) v += w;
+        }
+        if (t == 63) s_w0 = v;
     }
     __syncthreads();
-    for (int o = 1; o < kQ; o <<= 1) {
-        float add = 0.f;
-        if (t < kQ && t >= o) add = s_cs[t - o];
-        __syncthreads();
-        if (t < kQ) s_cs[t] += add;
-        __syncthreads();
-    }
     if (t < kQ) {
-        a.chunk_cs[((int64_t)c * a.n_heads + h) * kQ + t] = s_cs[t];
-        a.chunk_dt[((int64_t)c * a.n_heads + h) * kQ + t] = s_dt[t];
+        if (t >= 64) v += s_w0;
+        s_dt[t] = dt;
+        s_cs[t] = v;
+        a.chunk_cs[((int64_t)c * a.n_heads + h) * kQ + t] = v;
+        a.chunk_dt[((int64_t)c * a.n_heads + h) * kQ + t] = dt;
     }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- chunk states
@@ -79,30 +83,42 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(const PrefillArgs a
     __shared__ __attribute__((aligned(16))) uint16_t s_xl[kHP * kLd];   // (w_s x_s)^T lo
     __shared__ __attribute__((aligned(16))) uint16_t s_bt[kDS * kLd];   // B^T [n][s]
 
-    chunk_decay(a, c, h, tok0, L, s_dt, s_cs);
-    __syncthreads();
-    const float cs_end = s_cs[L - 1];
-    for (int e = t; e < kQ * (kHP / 8); e += kThreads) {
-        const int s = e & (kQ - 1), p8 = e >> 7;
-        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (s < L) {
-            unpack8(*reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8), f);
-            const float ws = __expf(cs_end - s_cs[s]) * s_dt[s];
+    // All global loads first (rows past the chunk's end read its last row and are zeroed
+    // when stored), then the decay scan, then the LDS stores.
+    constexpr int kXI = kQ * (kHP / 8) / kThreads, kBI = kQ * (kDS / 8) / kThreads;
+    uint4 xv[kXI], bv[kBI];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) f[j] *= ws;
-        }
+    for (int i = 0; i < kXI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), p8 = e >> 7;
+        xv[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (s < L ? s : L - 1)) * a.conv_dim + h * kHP + p8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), n8 = e >> 7;
+        bv[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (s < L ? s : L - 1)) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
+    }
+    const int tr = t < L ? t : L - 1;
+    const float u = bf16_to_f32(a.zxbcdt[(tok0 + tr) * a.d_in_proj + a.dt_off + h]);
+    chunk_decay(a, c, h, L, u, s_dt, s_cs);
+    const float cs_end = s_cs[L - 1];
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), p8 = e >> 7;
+        float f[8];
+        unpack8(xv[i], f);
+        const float ws = s < L ? __expf(cs_end - s_cs[s]) * s_dt[s] : 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             __bf16 hi, lo;
-            split_bf16(f[j], hi, lo);
+            split_bf16(s < L ? f[j] * ws : 0.f, hi, lo);
             s_xh[(p8 * 8 + j) * kLd + s] = bits(hi);
             s_xl[(p8 * 8 + j) * kLd + s] = bits(lo);
         }
     }
-    for (int e = t; e < kQ * (kDS / 8); e += kThreads) {
-        const int s = e & (kQ - 1), n8 = e >> 7;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), n8 = e >> 7;
+        const uint4 v = s < L ? bv[i] : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -156,16 +172,50 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
     __shared__ __attribute__((aligned(16))) uint16_t s_hh[kHP * kLd];      // H_in hi [p][n]
     __shared__ __attribute__((aligned(16))) uint16_t s_hl[kHP * kLd];      // H_in lo [p][n]
 
+    const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
+    const int ti = wave;
+    const int trow = 16 * ti + r16;                   // this lane's row t
+    const bool tok = trow < L;
+
+    // Every global load of the staging, and this wave's C rows, is issued before the first
+    // LDS store (a load-store loop would pay one memory latency per iteration). Rows past
+    // the chunk's end are read from its last row (always in bounds) and zeroed.
+    constexpr int kXI = kQ * (kHP / 8) / kThreads, kBI = kQ * (kDS / 8) / kThreads, kHI = kHP * kDS / 4 / kThreads;
+    uint4 xv[kXI], bv[kBI];
+    float4 hv[kHI];
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), p8 = e >> 7;
+        xv[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (s < L ? s : L - 1)) * a.conv_dim + h * kHP + p8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+        const int e = t + i * kThreads, s = e >> 4, n8 = e & 15;
+        bv[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (s < L ? s : L - 1)) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
+    }
+    const float4* hin = reinterpret_cast<const float4*>(a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS);
+#pragma unroll
+    for (int i = 0; i < kHI; ++i) hv[i] = hin[t + i * kThreads];
+    const uint16_t* crow = a.xbc_conv + (tok0 + (tok ? trow : L - 1)) * a.conv_dim + a.c_off + g * kDS + q * 8;
+    bf16x8 cop[kDS / 32];                             // C[t][k-step]
+#pragma unroll
+    for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = *reinterpret_cast<const bf16x8*>(crow + kn * 32);
     const float* cs_in = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
     const float* dt_in = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
+    float csv = 0.f, dtv = 0.f;
     if (t < kQ) {
-        s_cs[t] = cs_in[t];
-        s_dt[t] = dt_in[t];
+        csv = cs_in[t];
+        dtv = dt_in[t];
     }
-    for (int e = t; e < kQ * (kHP / 8); e += kThreads) {
-        const int s = e & (kQ - 1), p8 = e >> 7;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + h * kHP + p8 * 8);
+
+    if (t < kQ) {
+        s_cs[t] = csv;
+        s_dt[t] = dtv;
+    }
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) {
+        const int e = t + i * kThreads, s = e & (kQ - 1), p8 = e >> 7;
+        const uint4 v = s < L ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -173,39 +223,31 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
             s_xt[(p8 * 8 + 2 * j + 1) * kLd + s] = (uint16_t)(w[j] >> 16);
         }
     }
-    for (int e = t; e < kQ * (kDS / 8); e += kThreads) {
-        const int s = e >> 4, n8 = e & 15;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s < L) v = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + s) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
-        *reinterpret_cast<uint4*>(&s_b[s * kLd + n8 * 8]) = v;
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+        const int e = t + i * kThreads, s = e >> 4, n8 = e & 15;
+        *reinterpret_cast<uint4*>(&s_b[s * kLd + n8 * 8]) = s < L ? bv[i] : make_uint4(0u, 0u, 0u, 0u);
     }
-    {
-        const float4* hin = reinterpret_cast<const float4*>(a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS);
-        for (int e = t; e < kHP * kDS / 4; e += kThreads) {
-            const int p = e >> 5, n4 = (e & 31) * 4;
-            const float4 v = hin[e];
-            __bf16 hi[4], lo[4];
-            split_bf16(v.x, hi[0], lo[0]);
-            split_bf16(v.y, hi[1], lo[1]);
-            split_bf16(v.z, hi[2], lo[2]);
-            split_bf16(v.w, hi[3], lo[3]);
-            *reinterpret_cast<uint2*>(&s_hh[p * kLd + n4]) =
-                make_uint2(bits(hi[0]) | ((uint32_t)bits(hi[1]) << 16), bits(hi[2]) | ((uint32_t)bits(hi[3]) << 16));
-            *reinterpret_cast<uint2*>(&s_hl[p * kLd + n4]) =
-                make_uint2(bits(lo[0]) | ((uint32_t)bits(lo[1]) << 16), bits(lo[2]) | ((uint32_t)bits(lo[3]) << 16));
-        }
+#pragma unroll
+    for (int i = 0; i < kHI; ++i) {
+        const int e = t + i * kThreads, p = e >> 5, n4 = (e & 31) * 4;
+        const float4 v = hv[i];
+        __bf16 hi[4], lo[4];
+        split_bf16(v.x, hi[0], lo[0]);
+        split_bf16(v.y, hi[1], lo[1]);
+        split_bf16(v.z, hi[2], lo[2]);
+        split_bf16(v.w, hi[3], lo[3]);
+        *reinterpret_cast<uint2*>(&s_hh[p * kLd + n4]) =
+            make_uint2(bits(hi[0]) | ((uint32_t)bits(hi[1]) << 16), bits(hi[2]) | ((uint32_t)bits(hi[3]) << 16));
+        *reinterpret_cast<uint2*>(&s_hl[p * kLd + n4]) =
+            make_uint2(bits(lo[0]) | ((uint32_t)bits(lo[1]) << 16), bits(lo[2]) | ((uint32_t)bits(lo[3]) << 16));
+    }
+    if (!tok) {
+#pragma unroll
+        for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = bf16x8{};
     }
     __syncthreads();
-
-    const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
-    const int ti = wave;
     if (16 * ti >= L) return;
-    const int trow = 16 * ti + r16;                   // this lane's row t
-    const bool tok = trow < L;
-    const uint16_t* crow = a.xbc_conv + (tok0 + trow) * a.conv_dim + a.c_off + g * kDS + q * 8;
-    bf16x8 cop[kDS / 32];                             // C[t][k-step]
-#pragma unroll
-    for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = tok ? *reinterpret_cast<const bf16x8*>(crow + kn * 32) : bf16x8{};
     const float cs_t = s_cs[trow];
 
     v4f acc1[4], acc2[4];
