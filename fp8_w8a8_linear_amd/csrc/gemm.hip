@@ -16,8 +16,15 @@
 //    one XCD so the panel is fetched into that XCD's L2 once. Loads go through
 //    buffer descriptors, whose range check returns zeros past the operand's end,
 //    so ragged edges and padded steps need no branches in the loop.
-//  * tile kernel (larger m): 128 x 128 workgroup tiles, both operands staged
-//    through double-buffered LDS, four waves of 64 x 64.
+//  * 256 x 256 tile kernel (enough tiles to fill the chip): both operand tiles
+//    stream into a five-stage LDS ring by direct-to-LDS buffer loads (no register
+//    round trip; the range check zero-fills ragged rows and k), eight waves of
+//    128 x 64 on the 32x32x64 MFMA read the operands of the next stage while the
+//    MFMAs of the current one run, and the bf16 result leaves through LDS so that
+//    every store writes whole output rows. The wide tile halves the operand bytes
+//    per MAC of a 128 x 128 tile, which is what bounds this GEMM on the L2 -> CU path.
+//  * 128 x 128 tile kernel (remaining shapes): both operands staged through
+//    double-buffered LDS, four waves of 64 x 64.
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -300,6 +307,210 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tile kernel
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWT = 256;               // workgroup tile, n and m
+constexpr int kWK = 64;                // k bytes per ring stage (one 32x32x64 MFMA deep)
+constexpr int kRing = 5;               // ring stages: 5 x 32 KB fills the 160 KB LDS
+constexpr int kOpStage = kWT * kWK;    // one operand's stage, 16 KB
+constexpr int kStage = 2 * kOpStage;
+
+__device__ __forceinline__ v16f mfma32_e4m3(const v8i& a, const v8i& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Two floats to packed bf16 by the hardware conversion: round half to even, equal to
+// f32_to_bf16 on every non-NaN input (checked over all 2^32 bit patterns); NaN stays NaN.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// 64-byte LDS rows; the 16-byte chunk c of row r sits at slot c ^ (((r >> 1) ^ (r >> 2)) & 3),
+// so 16 consecutive rows read at one chunk (a 64-lane b128 read serves 16 lanes per pass)
+// cover all 16 slots of the 256-byte bank window, and 8 consecutive rows all 8 of 128 bytes.
+__device__ __forceinline__ int swz64(int row, int c) { return row * 64 + ((c ^ (((row >> 1) ^ (row >> 2)) & 3)) << 4); }
+
+// Buffer descriptor over [base, base + bytes) (bytes clamped to 2^31 - 1) with range checking.
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)b;
+    r[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
+    r[2] = (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from byte offset voff of the buffer into LDS at lds + 16 * lane (an
+// offset past the range writes zeros). Issued as asm so that the compiler's wait insertion
+// does not hold every later LDS read behind it; the kernel waits for these loads itself.
+__device__ __forceinline__ void dma16(const i32x4& rs, const uint8_t* lds, uint32_t voff) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rs)
+                 : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt <= n (n < 64), expcnt and lgkmcnt left alone
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Operands under 2^31 bytes (buffer offsets). Grid = number of 256 x 256 tiles, 512 threads.
+__global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
+    static_assert(kRing * kStage >= kWT * kWT * 2, "the epilogue stages the whole bf16 tile in the ring");
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n 128 x m 64
+    const int r32 = lane & 31, q = lane >> 5;
+
+    // Blocks go to the 8 XCDs round robin; each XCD takes a contiguous share of the tiles in an
+    // order that walks 8 m-tiles per n-tile, so the ~32 tiles an XCD holds at once share 8
+    // activation and 4 weight panels through its L2.
+    const int ntn = (int)((g.n + kWT - 1) / kWT), ntm = (int)((g.m + kWT - 1) / kWT);
+    const int total = ntn * ntm;
+    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int j = x * (total >> 3) + min(x, total & 7) + loc;
+    constexpr int kGroupM = 8;
+    const int grp = j / (kGroupM * ntn), within = j - grp * kGroupM * ntn;
+    const int gms = min(kGroupM, ntm - grp * kGroupM);
+    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * kWT, n0 = (int64_t)(within / gms) * kWT;
+
+    // DMA: wave w fills rows 32 w .. 32 w + 31 of both operand tiles of a stage, 16 rows per
+    // instruction; lane l lands in slot l of the instruction's 1 KB: row 16 i + l / 4, chunk
+    // slot l % 4, which holds the logical chunk kc / 16 under the swizzle.
+    const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
+    const int lr = lane >> 2;
+    const int kc = ((lane & 3) ^ (((lr >> 1) ^ (lr >> 2)) & 3)) * 16;
+    uint32_t wb[2], ab[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = wave * 32 + i * 16 + lr;
+        wb[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
+        ab[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
+    }
+    auto issue = [&](int s) {   // stage s (s may run past k: its loads are out of range, zeros)
+        const uint32_t k0 = (uint32_t)s * kWK;
+        const bool kin = (int64_t)k0 + kc < g.k;
+        uint8_t* sb = smem + (s % kRing) * kStage + wave * 2048;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            dma16(wrs, sb + i * 1024, kin ? wb[i] + k0 : kOutOfRange);
+            dma16(ars, sb + kOpStage + i * 1024, kin ? ab[i] + k0 : kOutOfRange);
+        }
+    };
+    auto read_ops = [&](int s, v8i (&wop)[4], v8i (&aop)[2]) {
+        const uint8_t* sw = smem + (s % kRing) * kStage;
+        const uint8_t* sa = sw + kOpStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wn * 128 + i * 32 + r32;
+            wop[i] = cat8(lds16(sw + swz64(row, 2 * q)), lds16(sw + swz64(row, 2 * q + 1)));
+        }
+#pragma unroll
+        for (int jx = 0; jx < 2; ++jx) {
+            const int row = wm * 64 + jx * 32 + r32;
+            aop[jx] = cat8(lds16(sa + swz64(row, 2 * q)), lds16(sa + swz64(row, 2 * q + 1)));
+        }
+    };
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jx = 0; jx < 2; ++jx)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
+
+    const int nk = (int)((g.k + kWK - 1) / kWK);
+    // Step kt: wait for stage kt + 1 (this thread's loads), barrier (all of them landed, and
+    // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
+    // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
+    // stage kt (read one step earlier) run.
+    auto step = [&](int kt, const v8i (&cw)[4], const v8i (&ca)[2], v8i (&nw)[4], v8i (&na)[2]) {
+        wait_vmcnt<(kRing - 3) * 4>();
+        __syncthreads();
+        issue(kt + kRing - 1);
+        if (kt + 1 < nk) read_ops(kt + 1, nw, na);
+        __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jx = 0; jx < 2; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
+        __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
+    };
+#pragma unroll
+    for (int s = 0; s < kRing - 1; ++s) issue(s);
+    v8i w0[4], a0[2], w1[4], a1[2];
+    wait_vmcnt<(kRing - 2) * 4>();
+    __syncthreads();
+    read_ops(0, w0, a0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, w0, a0, w1, a1);
+        step(kt + 1, w1, a1, w0, a0);
+    }
+    if (kt < nk) step(kt, w0, a0, w1, a1);
+    wait_vmcnt<0>();   // the ring's trailing loads (past k) before the ring is reused
+
+    // acc[i][jx] register r: n = 32 i + 8 (r / 4) + 4 q + r % 4, m = 32 jx + lane % 32 (wave
+    // tile relative). The scaled bf16 tile is staged in LDS as [m][n] with 512-byte rows, the
+    // 16-byte chunk cn of row ml at slot cn ^ (ml & 15) with its two 8-byte halves swapped when
+    // bit 3 xor bit 4 of ml is set: the 8-byte writes of 32 rows at one n land in 32 distinct
+    // slots of the 256-byte bank window. Each half-wave then stores one whole 512-byte row.
+    __syncthreads();   // every wave is done reading the ring
+    const float sa = *g.a_scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int nl = wn * 128 + i * 32 + gq * 8;
+            const int64_t nb = n0 + nl + q * 4;
+            float sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
+#pragma unroll
+            for (int jx = 0; jx < 2; ++jx) {
+                const int ml = wm * 64 + jx * 32 + r32;
+                const int hs = ((ml >> 3) ^ (ml >> 4)) & 1;
+                *reinterpret_cast<uint2*>(smem + ml * 512 + (((nl >> 3) ^ (ml & 15)) << 4) + ((q ^ hs) << 3)) =
+                    make_uint2(pk_bf16(acc[i][jx][4 * gq] * sc[0], acc[i][jx][4 * gq + 1] * sc[1]),
+                               pk_bf16(acc[i][jx][4 * gq + 2] * sc[2], acc[i][jx][4 * gq + 3] * sc[3]));
+            }
+        }
+    __syncthreads();
+    const bool vec = (g.ld_out & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+    const bool full = vec && m0 + kWT <= g.m && n0 + kWT <= g.n;
+#pragma unroll 4
+    for (int it = 0; it < kWT * kWT / 8 / 512; ++it) {
+        const int e = t + it * 512, ml = e >> 5, cn = e & 31;
+        uint4 v = lds16(smem + ml * 512 + ((cn ^ (ml & 15)) << 4));
+        if (((ml >> 3) ^ (ml >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        const int64_t mm = m0 + ml, nn = n0 + cn * 8;
+        uint16_t* o = g.out + mm * g.ld_out + nn;
+        if (full) {
+            *reinterpret_cast<uint4*>(o) = v;
+        } else if (mm < g.m) {
+            if (vec && nn + 8 <= g.n) {
+                *reinterpret_cast<uint4*>(o) = v;
+            } else {
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (nn + c < g.n) o[c] = (uint16_t)(w4[c >> 1] >> (16 * (c & 1)));
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <int BM, int WN>
@@ -311,7 +522,10 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
 // panel kernel with 128 x 192 tiles takes in_proj from 37 to 33 us; where those
 // tiles give too few workgroups to fill the chip (out_proj: 56), 64 x 128 tiles
-// (168 workgroups) take it from 34 to 21 us. From m = 4096 up the tile kernel leads.
+// (168 workgroups) take it from 34 to 21 us. The 256 x 256 kernel leads from about
+// 160 of its tiles (m = 1024 for in_proj, m = 4096 for out_proj: 45 vs 54 us and
+// 60 vs 74 us; at m = 15,360 477 vs 652 us and 187 vs 253 us) and trails below
+// (123 tiles at m = 641: 43 vs 36 us).
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        hipStream_t st) {
@@ -326,6 +540,11 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         else
             launch_panel<64, 32>(g, st);
         return check_launch("gemm (panel)");
+    }
+    const int64_t wide_tiles = ((n + kWT - 1) / kWT) * ((m + kWT - 1) / kWT);
+    if (offsets_fit && wide_tiles >= 160) {
+        tile256_kernel<<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
+        return check_launch("gemm (256 x 256)");
     }
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));
     if (offsets_fit)

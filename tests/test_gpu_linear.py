@@ -67,10 +67,13 @@ def test_linear_sweep_shapes(nhm, m, n, k):
 
 
 # m <= 16: GEMV; m <= 640: panel kernel (128 x 192 tiles when they give >= 160 workgroups,
-# else 64 x 128); larger m: tile kernel. The ragged shapes cut every kind of tile edge.
+# else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160 tiles (the last two
+# shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
+# x 272: partial m and n tiles, n % 8 != 0, k ending inside a 64-byte ring stage).
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
                                    (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
-                                   (500, 10000, 2672), (641, 130, 256), (700, 520, 272)])
+                                   (500, 10000, 2672), (641, 130, 256), (700, 520, 272),
+                                   (2600, 4100, 272), (1030, 10304, 2688)])
 def test_linear_ragged(nhm, m, n, k):
     from workloads import linear_case
     a, w, ws, sa = linear_case(m, n, k, extra=7)
@@ -93,13 +96,24 @@ def test_linear_strided_output(nhm, m, ld_pad):
     _check(nhm, a, w, ws, sa, ld_pad=ld_pad)
 
 
-def test_linear_large_m(nhm):
+# (1024, 2688, 4096): 128 x 128 tiles; (4096, 2688, 4096): 176 tiles of 256 x 256
+@pytest.mark.parametrize("m", [1024, 4096])
+def test_linear_large_m(nhm, m):
     from workloads import linear_case
-    a, w, ws, sa = linear_case(1024, 2688, 4096, extra=5)
+    a, w, ws, sa = linear_case(m, 2688, 4096, extra=5)
     _check(nhm, a, w, ws, sa)
 
 
-@pytest.mark.parametrize("m", [8, 200, 512, 700])
+# the 256 x 256 tile kernel's output staging with a padded row stride: 4112 keeps 16-byte
+# stores, 4113 takes the element path
+@pytest.mark.parametrize("ld_pad", [12, 13])
+def test_linear_strided_output_wide_tiles(nhm, ld_pad):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(2600, 4100, 272, extra=6)
+    _check(nhm, a, w, ws, sa, ld_pad=ld_pad)
+
+
+@pytest.mark.parametrize("m", [8, 200, 512, 700, 4096])
 def test_linear_deterministic(nhm, m):
     from tests.gpu_util import dev, host
     from workloads import linear_case
