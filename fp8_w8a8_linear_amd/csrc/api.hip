@@ -358,6 +358,8 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     const MixerWs w = prefill_ws(&p->g, n_tokens, n_seqs, chunk);
     if (ws_bytes < w.pub.total)
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
+    if ((int64_t)w.max_chunks * p->g.n_heads > INT32_MAX)   // one scan block per (chunk, head)
+        return fail(NHM_ERR_UNSUPPORTED, "%d chunks x %d heads exceed the scan's grid", w.max_chunks, p->g.n_heads);
     hipStream_t st = (hipStream_t)stream;
     char* wsb = static_cast<char*>(ws);
     const int64_t H = p->g.hidden;

@@ -71,16 +71,35 @@ __device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, 
 
 // ---------------------------------------------------------------- chunk states
 
-__global__ __launch_bounds__(kThreads) void ssd_state_kernel(const PrefillArgs a) {
-    const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+// Block -> (chunk, head) for the 1-D grid of max_chunks x n_heads blocks: the heads of a
+// chunk are consecutive blocks, so they share the chunk's dt rows (one line holds every
+// head's dt of a token) and B / C rows while those are in L2. Blocks go to the 8 XCDs round
+// robin; with n_heads % 8 == 0 XCD x takes the contiguous heads x n_heads/8 .. + n_heads/8 - 1,
+// whole groups when n_groups divides 8, so a group's B and C are fetched into one L2.
+__device__ __forceinline__ void chunk_head(const PrefillArgs& a, int& c, int& h) {
+    const int b = blockIdx.x, r = b % a.n_heads;
+    c = b / a.n_heads;
+    h = (a.n_heads & 7) ? r : (r & 7) * (a.n_heads >> 3) + (r >> 3);
+}
+
+
+// S_c = (w x)^T B with w_s = exp(cs_end - cs_s) dt_s. x^T and B^T are staged as they are
+// (bf16, exact) with w in LDS; a wave forms its A operand w_s x_s[p] in f32 and splits it
+// into bf16 hi + lo in registers. Wave w owns p-tile w % 4 and n-tiles 4 (w / 4) .. + 3, so
+// each operand is formed once and serves four MFMA pairs. 53 KB of LDS: three workgroups
+// share a CU.
+__global__ __launch_bounds__(kThreads, 6) void ssd_state_kernel(const PrefillArgs a) {
+    const int t = threadIdx.x;
+    int c, h;
+    chunk_head(a, c, h);
     const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
     if (info.x < 0) return;
     const int64_t tok0 = info.y;
     const int L = info.z;
     const int g = h / (a.n_heads / a.n_groups);
     __shared__ float s_cs[kQ], s_dt[kQ];
-    __shared__ __attribute__((aligned(16))) uint16_t s_xh[kHP * kLd];   // (w_s x_s)^T hi  [p][s]
-    __shared__ __attribute__((aligned(16))) uint16_t s_xl[kHP * kLd];   // (w_s x_s)^T lo
+    __shared__ __attribute__((aligned(16))) float s_w[kQ];                // w_s, zero beyond L
+    __shared__ __attribute__((aligned(16))) uint16_t s_xt[kHP * kLd];   // x^T [p][s]
     __shared__ __attribute__((aligned(16))) uint16_t s_bt[kDS * kLd];   // B^T [n][s]
 
     // All global loads first (rows past the chunk's end read its last row and are zeroed
@@ -101,18 +120,16 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(const PrefillArgs a
     const float u = bf16_to_f32(a.zxbcdt[(tok0 + tr) * a.d_in_proj + a.dt_off + h]);
     chunk_decay(a, c, h, L, u, s_dt, s_cs);
     const float cs_end = s_cs[L - 1];
+    if (t < kQ) s_w[t] = t < L ? __expf(cs_end - s_cs[t]) * s_dt[t] : 0.f;
 #pragma unroll
     for (int i = 0; i < kXI; ++i) {
         const int e = t + i * kThreads, s = e & (kQ - 1), p8 = e >> 7;
-        float f[8];
-        unpack8(xv[i], f);
-        const float ws = s < L ? __expf(cs_end - s_cs[s]) * s_dt[s] : 0.f;
+        const uint4 v = s < L ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __bf16 hi, lo;
-            split_bf16(s < L ? f[j] * ws : 0.f, hi, lo);
-            s_xh[(p8 * 8 + j) * kLd + s] = bits(hi);
-            s_xl[(p8 * 8 + j) * kLd + s] = bits(lo);
+        for (int j = 0; j < 4; ++j) {
+            s_xt[(p8 * 8 + 2 * j) * kLd + s] = (uint16_t)(w[j] & 0xffffu);
+            s_xt[(p8 * 8 + 2 * j + 1) * kLd + s] = (uint16_t)(w[j] >> 16);
         }
     }
 #pragma unroll
@@ -128,39 +145,58 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(const PrefillArgs a
     }
     __syncthreads();
 
-    // S[p][n]: 4 p-tiles x 8 n-tiles; wave w owns n-tile w
     const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
+    const int pt = wave & 3, nt0 = (wave >> 2) * 4;
     const int nks = (L + 31) / 32;
     v4f acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int ks = 0; ks < nks; ++ks) {
         const int koff = ks * 32 + q * 8;
-        const bf16x8 b0 = lds8(&s_bt[(16 * wave + r16) * kLd + koff]);
+        // A operand: w_s x_s[p] for p = 16 pt + r16 and the eight s at koff, split hi + lo
+        const uint4 xr = *reinterpret_cast<const uint4*>(&s_xt[(16 * pt + r16) * kLd + koff]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&s_w[koff]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&s_w[koff + 4]);
+        float f[8];
+        unpack8(xr, f);
+        const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        bf16x8 ah, al;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] = mfma_bf16(lds8(&s_xh[(16 * i + r16) * kLd + koff]), b0, acc[i]);
-            acc[i] = mfma_bf16(lds8(&s_xl[(16 * i + r16) * kLd + koff]), b0, acc[i]);
+        for (int j = 0; j < 8; ++j) {
+            __bf16 hi, lo;
+            split_bf16(f[j] * ws[j], hi, lo);
+            ah[j] = hi;
+            al[j] = lo;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 b = lds8(&s_bt[(16 * (nt0 + j) + r16) * kLd + koff]);
+            acc[j] = mfma_bf16(ah, b, acc[j]);
+            acc[j] = mfma_bf16(al, b, acc[j]);
         }
     }
     float* out = a.chunk_state + ((int64_t)c * a.n_heads + h) * kHP * kDS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[(16 * i + 4 * q + r) * kDS + 16 * wave + r16] = acc[i][r];
+        for (int r = 0; r < 4; ++r) out[(16 * pt + 4 * q + r) * kDS + 16 * (nt0 + j) + r16] = acc[j][r];
 }
 
 // ---------------------------------------------------------------- chunk outputs
 
 // One workgroup of 8 waves per (chunk, head); wave w computes the output rows of
-// t-tile w. B, H_in (split hi | lo) and x^T are staged once per workgroup; the C
-// rows of a wave's t-tile are read from L2 into registers and serve as the B
-// operand of C.B^T and the A operand of C.H_in^T. G never leaves registers: C.B^T
+// t-tile w. B and x^T are staged once per workgroup for G.x; H_in (split hi | lo),
+// loaded into registers at the start, then takes B's place in LDS for C.H_in^T, so a
+// workgroup holds 53 KB and three share a CU. The C rows of a wave's t-tile are read
+// from L2 into registers and serve as the B operand of C.B^T and the A operand of
+// C.H_in^T. G never leaves registers: C.B^T
 // is computed transposed (B as the A operand), so a lane holds G for one row t and
 // four consecutive s of each 16-wide s-tile -- an A operand of G.x once x is read
 // for the same eight s.
-__global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) {
-    const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs a) {   // 6 waves per SIMD: 3 workgroups per CU
+    const int t = threadIdx.x;
+    int c, h;
+    chunk_head(a, c, h);
     const int4 info = reinterpret_cast<const int4*>(a.chunk_info)[c];
     if (info.x < 0) return;
     const int64_t tok0 = info.y;
@@ -168,9 +204,11 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
     const int g = h / (a.n_heads / a.n_groups);
     __shared__ float s_cs[kQ], s_dt[kQ];
     __shared__ __attribute__((aligned(16))) uint16_t s_xt[kHP * kLd];      // x^T [p][s]
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[kQ * kLd];        // B [s][n]
-    __shared__ __attribute__((aligned(16))) uint16_t s_hh[kHP * kLd];      // H_in hi [p][n]
-    __shared__ __attribute__((aligned(16))) uint16_t s_hl[kHP * kLd];      // H_in lo [p][n]
+    // B [s][n] for G x; afterwards the same bytes hold H_in hi and lo [p][n] for C H_in^T
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[kQ * kLd];
+    static_assert(2 * kHP * kLd <= kQ * kLd, "H_in hi and lo fit where B was");
+    uint16_t* const s_hh = s_b;
+    uint16_t* const s_hl = s_b + kHP * kLd;
 
     const int lane = t & 63, wave = t >> 6, r16 = lane & 15, q = lane >> 4;
     const int ti = wave;
@@ -228,6 +266,60 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
         const int e = t + i * kThreads, s = e >> 4, n8 = e & 15;
         *reinterpret_cast<uint4*>(&s_b[s * kLd + n8 * 8]) = s < L ? bv[i] : make_uint4(0u, 0u, 0u, 0u);
     }
+    if (!tok) {
+#pragma unroll
+        for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = bf16x8{};
+    }
+    __syncthreads();
+    const bool live = 16 * ti < L;                    // wave-uniform: this t-tile has rows
+    const float cs_t = s_cs[trow];
+
+    v4f acc1[4], acc2[4];
+#pragma unroll
+    for (int pj = 0; pj < 4; ++pj) acc1[pj] = acc2[pj] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (live) {
+        // y1 = G x over the 32-wide s blocks kk with 32 kk <= 16 ti + 15
+        const int nkk = (16 * ti + 15) / 32 + 1;
+        for (int kk = 0; kk < nkk; ++kk) {
+            float gv[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int sj = 2 * kk + half;               // s-tile
+                v4f cb = {0.f, 0.f, 0.f, 0.f};
+                if (sj <= ti) {
+#pragma unroll
+                    for (int kn = 0; kn < kDS / 32; ++kn)
+                        cb = mfma_bf16(lds8(&s_b[(16 * sj + r16) * kLd + kn * 32 + q * 8]), cop[kn], cb);
+                }
+                // cb[r] = (C.B^T)[t = trow][s = 16 sj + 4 q + r]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sc = 16 * sj + 4 * q + r;
+                    gv[4 * half + r] = (sc <= trow && tok) ? cb[r] * __expf(cs_t - s_cs[sc]) * s_dt[sc] : 0.f;
+                }
+            }
+            bf16x8 gh, gl;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __bf16 hi, lo;
+                split_bf16(gv[j], hi, lo);
+                gh[j] = hi;
+                gl[j] = lo;
+            }
+            // B operand: x[s][p] for the same eight s, p = 16 pj + r16
+#pragma unroll
+            for (int pj = 0; pj < 4; ++pj) {
+                const uint16_t* xr = &s_xt[(16 * pj + r16) * kLd + 32 * kk + 4 * q];
+                const uint2 lo = *reinterpret_cast<const uint2*>(xr);
+                const uint2 hi = *reinterpret_cast<const uint2*>(xr + 16);
+                const bf16x8 xb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc1[pj] = mfma_bf16(gh, xb, acc1[pj]);
+                acc1[pj] = mfma_bf16(gl, xb, acc1[pj]);
+            }
+        }
+    }
+    __syncthreads();   // every wave is done with B
 #pragma unroll
     for (int i = 0; i < kHI; ++i) {
         const int e = t + i * kThreads, p = e >> 5, n4 = (e & 31) * 4;
@@ -242,57 +334,8 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
         *reinterpret_cast<uint2*>(&s_hl[p * kLd + n4]) =
             make_uint2(bits(lo[0]) | ((uint32_t)bits(lo[1]) << 16), bits(lo[2]) | ((uint32_t)bits(lo[3]) << 16));
     }
-    if (!tok) {
-#pragma unroll
-        for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = bf16x8{};
-    }
     __syncthreads();
-    if (16 * ti >= L) return;
-    const float cs_t = s_cs[trow];
-
-    v4f acc1[4], acc2[4];
-#pragma unroll
-    for (int pj = 0; pj < 4; ++pj) acc1[pj] = acc2[pj] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // y1 = G x over the 32-wide s blocks kk with 32 kk <= 16 ti + 15
-    const int nkk = (16 * ti + 15) / 32 + 1;
-    for (int kk = 0; kk < nkk; ++kk) {
-        float gv[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int sj = 2 * kk + half;               // s-tile
-            v4f cb = {0.f, 0.f, 0.f, 0.f};
-            if (sj <= ti) {
-#pragma unroll
-                for (int kn = 0; kn < kDS / 32; ++kn)
-                    cb = mfma_bf16(lds8(&s_b[(16 * sj + r16) * kLd + kn * 32 + q * 8]), cop[kn], cb);
-            }
-            // cb[r] = (C.B^T)[t = trow][s = 16 sj + 4 q + r]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int sc = 16 * sj + 4 * q + r;
-                gv[4 * half + r] = (sc <= trow && tok) ? cb[r] * __expf(cs_t - s_cs[sc]) * s_dt[sc] : 0.f;
-            }
-        }
-        bf16x8 gh, gl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __bf16 hi, lo;
-            split_bf16(gv[j], hi, lo);
-            gh[j] = hi;
-            gl[j] = lo;
-        }
-        // B operand: x[s][p] for the same eight s, p = 16 pj + r16
-#pragma unroll
-        for (int pj = 0; pj < 4; ++pj) {
-            const uint16_t* xr = &s_xt[(16 * pj + r16) * kLd + 32 * kk + 4 * q];
-            const uint2 lo = *reinterpret_cast<const uint2*>(xr);
-            const uint2 hi = *reinterpret_cast<const uint2*>(xr + 16);
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc1[pj] = mfma_bf16(gh, xb, acc1[pj]);
-            acc1[pj] = mfma_bf16(gl, xb, acc1[pj]);
-        }
-    }
+    if (!live) return;
     // y2 = C H_in^T
 #pragma unroll
     for (int pj = 0; pj < 4; ++pj) {
@@ -320,11 +363,11 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(const PrefillArgs a) 
 }
 
 void launch_ssd_state(const PrefillArgs& a, hipStream_t st) {
-    ssd_state_kernel<<<dim3(a.max_chunks, a.n_heads), kThreads, 0, st>>>(a);
+    ssd_state_kernel<<<dim3((unsigned)(a.max_chunks * a.n_heads)), kThreads, 0, st>>>(a);
 }
 
 void launch_ssd_out(const PrefillArgs& a, hipStream_t st) {
-    ssd_out_kernel<<<dim3(a.max_chunks, a.n_heads), kThreads, 0, st>>>(a);
+    ssd_out_kernel<<<dim3((unsigned)(a.max_chunks * a.n_heads)), kThreads, 0, st>>>(a);
 }
 
 }  // namespace nhm

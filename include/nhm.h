@@ -254,7 +254,9 @@ NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_
  * The projections follow nhm_fp8_linear (above 16 tokens the e4m3 MFMA GEMM); the
  * dt columns of in_proj, which every later token's decay exponentiates, are then
  * recomputed with exact f32 accumulation.
- * n_tokens == 0 with n_seqs == 0 is a valid no-op.
+ * n_tokens == 0 with n_seqs == 0 is a valid no-op. The scan runs one block per
+ * (chunk, head): (n_tokens / chunk + n_seqs) * g.n_heads above 2^31 - 1 is
+ * NHM_ERR_UNSUPPORTED.
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
  * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
 NHM_API nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,
