@@ -14,31 +14,39 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> bfloat16 bits, round half to even; NaN becomes a quiet NaN with its sign.
-// Both results are computed and one is selected, so the conversion never diverges.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t nan = ((u >> 16) & 0x8000u) | 0x7fc0u;
-    return (u & 0x7fffffffu) > 0x7f800000u ? nan : r;
+// float -> bfloat16 bits, round half to even (the hardware conversion; checked equal to
+// the integer rounding (u + 0x7fff + lsb) >> 16 on every non-NaN float); NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two floats to a dword of two bf16 (a in the low half), each as f32_to_bf16, in one instruction.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // float -> OCP FP8 E4M3FN code: round half to even, saturating at +-448 (infinities
-// included), NaN -> 0x7F with the sign kept, zero results keep the sign bit.
-// Integer form: for |v| in [2^-6, 448) the code is the float's biased exponent and
-// top three mantissa bits, rounded half to even on the 20 bits below them and
-// re-biased from 127 to 7; below 2^-6 the code counts multiples of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
+// included), NaN -> 0x7F with the sign kept, zero results keep the sign bit. The value is
+// clamped to [-448, 448] and converted by the hardware (round half to even); NaN is
+// selected separately. Checked on all 2^32 float bit patterns against the integer form:
+// for |v| in [2^-6, 448) the code is the float's biased exponent and top three mantissa
+// bits rounded half to even on the 20 bits below them and re-biased from 127 to 7, below
+// 2^-6 it counts multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_nan(float v, uint32_t code) {
     const uint32_t u = __float_as_uint(v);
-    const uint32_t s = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    // every branch is evaluated and selected (no divergence); the subnormal one on a clamped input
-    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a < 0x3c800000u ? a : 0x3c800000u) * 512.0f);
-    const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t c = a < 0x3c800000u ? sub : nrm;   // 2^-6
-    c = a >= 0x43e00000u ? 0x7eu : c;           // 448.0f and above, infinities
-    c = a > 0x7f800000u ? 0x7fu : c;            // NaN
-    return s | c;
+    return (u & 0x7fffffffu) > 0x7f800000u ? (((u >> 24) & 0x80u) | 0x7fu) : code;
+}
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+    return e4m3_nan(v, (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu);
+}
+// Four values to four codes (bytes in argument order), each as e4m3_code.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                            __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                                                  __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f), (int)r, true);
+    return e4m3_nan(a, r & 0xffu) | (e4m3_nan(b, (r >> 8) & 0xffu) << 8) | (e4m3_nan(c, (r >> 16) & 0xffu) << 16) |
+           (e4m3_nan(d, r >> 24) << 24);
 }
 
 // Exact float value of an e4m3 code (finite codes; the GEMMs never decode in software).
@@ -52,6 +60,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 __device__ __forceinline__ uint32_t quant_bf16(uint32_t xb, float s) {
     return e4m3_code(__fdiv_rn(bf16_to_f32(xb), s));
 }
+// Four bf16 values (two dwords, memory order) to four codes, each as quant_bf16.
+__device__ __forceinline__ uint32_t quant_bf16x4(uint32_t w0, uint32_t w1, float s) {
+    return e4m3x4(__fdiv_rn(bf16_to_f32(w0 & 0xffffu), s), __fdiv_rn(bf16_to_f32(w0 >> 16), s),
+                  __fdiv_rn(bf16_to_f32(w1 & 0xffffu), s), __fdiv_rn(bf16_to_f32(w1 >> 16), s));
+}
 
 // The eight bf16 values of a 16-byte load, in memory order.
 __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
@@ -63,7 +76,8 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
     }
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x * sigmoid(x) with the hardware reciprocal (about 1 ulp) instead of an IEEE division
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(__expf(u)); }
 

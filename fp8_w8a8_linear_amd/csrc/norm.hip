@@ -27,17 +27,12 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     auto emit = [&](int c, const float (&v)[8], float r) {
         float w[8];
         unpack8(*reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c), w);
-        uint32_t ob[8], q[2] = {0u, 0u};
+        uint32_t ob[4];   // bf16 pairs
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ob[j] = f32_to_bf16(v[j] * r * w[j]);
-            q[j >> 2] |= quant_bf16(ob[j], so) << (8 * (j & 3));
-        }
+        for (int j = 0; j < 4; ++j) ob[j] = f32x2_to_bf16x2(v[2 * j] * r * w[2 * j], v[2 * j + 1] * r * w[2 * j + 1]);
         const int64_t o = tok * a.d_inner + (int64_t)g * gw + c;
-        if (a.norm)
-            *reinterpret_cast<uint4*>(a.norm + o) =
-                make_uint4(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16), ob[4] | (ob[5] << 16), ob[6] | (ob[7] << 16));
-        *reinterpret_cast<uint2*>(a.q_out + o) = make_uint2(q[0], q[1]);
+        if (a.norm) *reinterpret_cast<uint4*>(a.norm + o) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        *reinterpret_cast<uint2*>(a.q_out + o) = make_uint2(quant_bf16x4(ob[0], ob[1], so), quant_bf16x4(ob[2], ob[3], so));
     };
     float ss = 0.f;
     if constexpr (kIt > 0) {

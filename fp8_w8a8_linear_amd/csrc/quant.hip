@@ -17,16 +17,7 @@ __global__ __launch_bounds__(256) void quant_vec8_kernel(const uint16_t* __restr
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / vec_per_row, v = i - r * vec_per_row;
         const uint4 in = *reinterpret_cast<const uint4*>(x + r * ld_x + v * 8);
-        const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            lo |= quant_bf16(w[j] & 0xffffu, s) << (16 * j);
-            lo |= quant_bf16(w[j] >> 16, s) << (16 * j + 8);
-            hi |= quant_bf16(w[j + 2] & 0xffffu, s) << (16 * j);
-            hi |= quant_bf16(w[j + 2] >> 16, s) << (16 * j + 8);
-        }
-        *reinterpret_cast<uint2*>(q + r * ld_q + v * 8) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(q + r * ld_q + v * 8) = make_uint2(quant_bf16x4(in.x, in.y, s), quant_bf16x4(in.z, in.w, s));
     }
 }
 
