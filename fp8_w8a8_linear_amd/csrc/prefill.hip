@@ -29,31 +29,33 @@ constexpr int kQ = 128;    // chunk length
 
 // Chunk c -> (sequence, first token, length, index within the sequence);
 // seq_chunk0[i] = first chunk of sequence i, seq_chunk0[n] = number of chunks.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int n, int Q,
-                                                    int max_chunks, int32_t* __restrict__ info,
-                                                    int32_t* __restrict__ seq_chunk0) {
-    __shared__ int s_scan[1024];
+// Run by one 256-thread block (the conv kernel's last block column, which the conv work
+// does not use; nothing in the conv reads the plan).
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ cu, int n, int Q, int max_chunks,
+                                           int32_t* __restrict__ info, int32_t* __restrict__ seq_chunk0) {
+    constexpr int kB = 256;
+    __shared__ int s_scan[kB];
     const int t = threadIdx.x;
     int carry = 0;
-    for (int base = 0; base < n; base += 1024) {
+    for (int base = 0; base < n; base += kB) {
         const int i = base + t;
         const int v = i < n ? (cu[i + 1] - cu[i] + Q - 1) / Q : 0;
         s_scan[t] = v;
         __syncthreads();
-        for (int o = 1; o < 1024; o <<= 1) {
+        for (int o = 1; o < kB; o <<= 1) {
             const int add = t >= o ? s_scan[t - o] : 0;
             __syncthreads();
             s_scan[t] += add;
             __syncthreads();
         }
         if (i < n) seq_chunk0[i] = carry + s_scan[t] - v;
-        carry += s_scan[1023];
+        carry += s_scan[kB - 1];
         __syncthreads();
     }
     if (t == 0) seq_chunk0[n] = carry;
     __syncthreads();
     const int total = carry;
-    for (int c = t; c < max_chunks; c += 1024) {
+    for (int c = t; c < max_chunks; c += kB) {
         int4 r = make_int4(-1, 0, 0, 0);
         if (c < total) {
             int lo = 0, hi = n - 1;            // last i with seq_chunk0[i] <= c
@@ -93,6 +95,10 @@ __device__ __forceinline__ uint4 init_row(const PrefillArgs& a, int i, int r, in
 // One thread: 8 channels x kConvRun consecutive tokens. The three previous rows
 // come from the same sequence or, before its first token, from its initial window.
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a) {
+    if (blockIdx.x == gridDim.x - 1) {     // the chunk plan, computed beside the conv
+        if (blockIdx.y == 0) plan_block(a.cu_seqlens, a.n_seqs, a.chunk, a.max_chunks, a.chunk_info, a.seq_chunk0);
+        return;
+    }
     const int c8 = blockIdx.x * 256 + threadIdx.x;
     if (c8 * 8 >= a.conv_dim) return;
     const int64_t t0 = (int64_t)blockIdx.y * kConvRun;
@@ -207,10 +213,10 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
 // ---------------------------------------------------------------- launcher
 
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
-    plan_kernel<<<1, 1024, 0, st>>>(a.cu_seqlens, a.n_seqs, a.chunk, a.max_chunks, a.chunk_info, a.seq_chunk0);
+    // conv blocks, plus one block column whose first block computes the chunk plan
     const int c8_blocks = (a.conv_dim / 8 + 255) / 256;
-    if (a.T > 0)
-        conv_fwd_kernel<<<dim3(c8_blocks, (unsigned)((a.T + kConvRun - 1) / kConvRun)), 256, 0, st>>>(a);
+    const int64_t tblocks = (a.T + kConvRun - 1) / kConvRun;
+    conv_fwd_kernel<<<dim3(c8_blocks + 1, (unsigned)(tblocks > 0 ? tblocks : 1)), 256, 0, st>>>(a);
     if (a.max_chunks > 0) launch_ssd_state(a, st);
     if (a.n_seqs > 0) ssd_pass_kernel<<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
     if (a.max_chunks > 0) launch_ssd_out(a, st);

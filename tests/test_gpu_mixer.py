@@ -269,6 +269,25 @@ def test_prefill_carry_split(nhm, block0):
     assert np.array_equal(cp2[0], cpw[0])
 
 
+def test_prefill_zero_tokens(nhm, block0):
+    """Only empty sequences: no token work, yet each pool row is carried through
+    (has_initial 1) or reset to the zero state and window (has_initial 0), as the oracle."""
+    from oracle import mixer_prefill
+    from tests.gpu_util import upload_params
+    from workloads import conv_pool, ssm_pool
+    S = 8
+    cu, sl, hi = [0, 0, 0], [6, 2], [1, 0]
+    h = np.zeros((0, H), np.uint16)
+    sp, cp = ssm_pool(4, 1, S), conv_pool(4, 1, S)
+    pd = upload_params(block0)
+    out, spg, cpg, _, _ = _gpu_prefill(nhm, pd, h, cu, sl, hi, sp, cp)
+    spr, cpr = sp.copy(), cp.copy()
+    mixer_prefill(block0, h, cu, sl, hi, spr, cpr)
+    assert out.shape == (0, H)
+    assert np.array_equal(spg, spr) and np.array_equal(cpg, cpr)
+    assert np.array_equal(spg[6], sp[6]) and not np.any(spg[2]) and not np.any(cpg[2])
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(1200)
 def test_prefill_ragged_15360_23_blocks(nhm):
