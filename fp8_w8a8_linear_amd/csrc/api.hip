@@ -369,15 +369,19 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
         if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, st)) != NHM_OK) return s;
-        // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every
-        // later token's decay exponentiates: its columns are recomputed with exact f32
-        // accumulation (the GEMV that serves small m accumulates exactly already)
-        if (!use_gemv(n_tokens, p->in_proj.n, p->in_proj.k) &&
-            (s = launch_exact_columns(q_in, H, n_tokens, p->in_proj.w, p->in_proj.w_scale, p->in_proj.a_scale,
-                                      p->in_proj.n, p->in_proj.k, l.dt_off, p->g.n_heads, zx, l.d_in_proj, st)) != NHM_OK)
-            return s;
     }
     PrefillArgs a;
+    // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every later
+    // token's decay exponentiates: its columns are recomputed with exact f32 accumulation in
+    // the conv launch (the GEMV that serves small m accumulates exactly already)
+    a.exact = n_tokens > 0 && !use_gemv(n_tokens, p->in_proj.n, p->in_proj.k);
+    if (a.exact && (p->in_proj.n * p->in_proj.k >= (int64_t(1) << 31) || n_tokens * H >= (int64_t(1) << 31)))
+        return fail(NHM_ERR_UNSUPPORTED, "prefill dt recompute: operands of 2 GiB or more");
+    a.q_in = q_in;
+    a.in_w = p->in_proj.w;
+    a.in_w_scale = p->in_proj.w_scale;
+    a.in_a_scale = p->in_proj.a_scale;
+    a.hidden = p->g.hidden;
     a.T = n_tokens;
     a.n_seqs = n_seqs;
     a.chunk = chunk;

@@ -27,19 +27,6 @@ struct GemvArgs {
     ConvEpilogue conv;
 };
 
-// 32 bytes of an operand row through a buffer descriptor: the descriptor's range check
-// returns zeros for offsets past the operand, so rows >= nrows and k beyond the end
-// need no branches (the caller passes kGemvOut for them).
-constexpr uint32_t kGemvOut = 0x80000000u;
-template <int kAux>
-__device__ __forceinline__ v8i bload32(const __amdgpu_buffer_rsrc_t& r, uint32_t lo_off, uint32_t hi_off) {
-    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(r, lo_off, 0, kAux);
-    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(r, hi_off, 0, kAux);
-    v8i v;
-    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-    return v;
-}
 constexpr int kStreamAux = 2;   // non-temporal: weight rows are read exactly once
 
 template <int kWaves, int kSteps, bool kConv>
@@ -165,81 +152,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         *reinterpret_cast<uint2*>(win + c.conv_dim) = w2;
         *reinterpret_cast<uint2*>(win + 2 * c.conv_dim) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
     }
-}
-
-// ---------------------------------------------------------------- exact columns
-// Recomputes output columns [c0, c0 + nc) of a W8A8 projection with exact f32
-// accumulation (bf16 MFMA on the converted codes), over all m rows. The mixer uses
-// it for the 64 dt columns of in_proj after the e4m3 GEMM: dt enters the scan through
-// exp(dt * A) of every later token, where one bf16 step of dt_raw moves a long-memory
-// head's state by up to a percent, so dt gets the accumulation the reference
-// prescribes rather than the e4m3 MFMA's coarser sum. A workgroup owns one 16 x 16
-// tile (16 rows, 16 columns); its 8 waves take the k-steps round robin with all their
-// loads in flight at once, and the partial tiles are summed through LDS in wave order,
-// as in the GEMV.
-constexpr int kExactWaves = 8, kExactSteps = 4;   // k-steps per wave per pass
-__global__ __launch_bounds__(kExactWaves * 64) void exact_columns_kernel(const GemvArgs g, int64_t c0, int64_t nc) {
-    __shared__ v4f s_red[kExactWaves][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * 16 + (lane & 15);                  // B operand row (token)
-    const int64_t cb = c0 + (int64_t)blockIdx.y * 16;
-    const int kq = (lane >> 4) * 32;
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
-    const uint32_t arow = t < g.m ? (uint32_t)(t * g.lda) : kGemvOut;
-    const int64_t cw = cb + (lane & 15);                                          // A operand row (column)
-    const uint32_t wrow = cw < c0 + nc ? (uint32_t)(cw * g.k) : kGemvOut;
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave; s0 < g.ksteps; s0 += kExactWaves * kExactSteps) {   // one pass for k <= 4096
-        v8i xb[kExactSteps], wa[kExactSteps];
-#pragma unroll
-        for (int i = 0; i < kExactSteps; ++i) {
-            const int s = s0 + i * kExactWaves;
-            const int kb = s * 128 + kq;
-            const bool in = s < g.ksteps && kb < g.k, in2 = s < g.ksteps && kb + 16 < g.k;
-            xb[i] = bload32<0>(ars, in ? arow + kb : kGemvOut, in2 ? arow + kb + 16 : kGemvOut);
-            wa[i] = bload32<0>(wrs, in ? wrow + kb : kGemvOut, in2 ? wrow + kb + 16 : kGemvOut);
-        }
-#pragma unroll
-        for (int i = 0; i < kExactSteps; ++i) {
-            if (s0 + i * kExactWaves >= g.ksteps) break;                      // wave-uniform
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
-                acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * sub], wa[i][2 * sub + 1]),
-                                e4m3x8_to_bf16(xb[i][2 * sub], xb[i][2 * sub + 1]), acc);
-        }
-    }
-    if (wave > 0) s_red[wave][lane] = acc;
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 1; w < kExactWaves; ++w) acc += s_red[w][lane];
-    // acc[r] = D[column cb + 4 (lane / 16) + r][token t]
-    if (t >= g.m) return;
-    const float sa = *g.a_scale;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t c = cb + 4 * (lane >> 4) + r;
-        if (c < c0 + nc) g.out[t * g.ld_out + c] = (uint16_t)f32_to_bf16(acc[r] * (sa * g.w_scale[c]));
-    }
-}
-
-nhm_status launch_exact_columns(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
-                                const float* a_scale, int64_t n, int64_t k, int64_t c0, int64_t nc, uint16_t* out,
-                                int64_t ld_out, hipStream_t st) {
-    if (m == 0 || nc == 0) return NHM_OK;
-    if (c0 < 0 || nc < 0 || c0 + nc > n) return fail(NHM_ERR_SHAPE, "exact columns [%lld, %lld) outside [0, %lld)",
-                                                     (long long)c0, (long long)(c0 + nc), (long long)n);
-    if (n * k >= (int64_t(1) << 31) || m * lda >= (int64_t(1) << 31))
-        return fail(NHM_ERR_UNSUPPORTED, "exact columns: operands of 2 GiB or more");
-    GemvArgs g{};
-    g.a = a; g.lda = lda; g.m = (int)m;
-    g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
-    g.out = out; g.ld_out = ld_out;
-    g.ksteps = (int)((k + 127) / 128);
-    const dim3 grid((unsigned)((m + 15) / 16), (unsigned)((nc + 15) / 16));
-    exact_columns_kernel<<<grid, dim3(kExactWaves * 64), 0, st>>>(g, c0, nc);
-    return check_launch("exact columns");
 }
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,

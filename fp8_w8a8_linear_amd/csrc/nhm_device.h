@@ -108,6 +108,19 @@ __device__ __forceinline__ v4f mfma_bf16(const bf16x8& a, const bf16x8& b, const
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32 bytes of an operand row through a buffer descriptor: the descriptor's range check
+// returns zeros for offsets past the operand, so rows >= nrows and k beyond the end
+// need no branches (the caller passes kGemvOut for them).
+constexpr uint32_t kGemvOut = 0x80000000u;
+template <int kAux>
+__device__ __forceinline__ v8i bload32(const __amdgpu_buffer_rsrc_t& r, uint32_t lo_off, uint32_t hi_off) {
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(r, lo_off, 0, kAux);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(r, hi_off, 0, kAux);
+    v8i v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return v;
+}
 // Eight e4m3 codes (two dwords, memory order) as exact bf16 values (hardware convert, scale 1).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);

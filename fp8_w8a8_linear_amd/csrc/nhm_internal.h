@@ -43,11 +43,6 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        const ConvEpilogue* conv, hipStream_t st);
 
-// Recomputes columns [c0, c0 + nc) of out = W8A8(a, w) with exact f32 accumulation (gemv.hip).
-nhm_status launch_exact_columns(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
-                                const float* a_scale, int64_t n, int64_t k, int64_t c0, int64_t nc, uint16_t* out,
-                                int64_t ld_out, hipStream_t st);
-
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
@@ -99,7 +94,7 @@ struct PrefillArgs {
     const float* dt_bias;
     const uint16_t* norm_w;
     const float* out_a_scale;
-    const uint16_t* zxbcdt;   // [T, d_in_proj]
+    uint16_t* zxbcdt;         // [T, d_in_proj] (its dt columns rewritten when exact)
     uint16_t* xbc_conv;       // [T, conv_dim]
     int32_t* chunk_info;      // [max_chunks, 4]: seq, tok0, len, index in seq
     int32_t* seq_chunk0;      // [n_seqs + 1]
@@ -109,8 +104,16 @@ struct PrefillArgs {
     uint16_t* y;              // [T, d_inner]
     uint16_t* norm;           // [T, d_inner] (nullptr: not kept)
     uint8_t* q_out;           // [T, d_inner]
+    // exact recompute of in_proj's dt columns (after the e4m3 GEMM; exact == 0: not needed)
+    int32_t exact;
+    const uint8_t* q_in;      // [T, hidden] e4m3 codes of the block input
+    const uint8_t* in_w;      // [d_in_proj, hidden] e4m3
+    const float* in_w_scale;  // [d_in_proj]
+    const float* in_a_scale;  // [1]
+    int32_t hidden;
 };
-// conv, chunked scan and the gated norm + quant, in stream order.
+// dt-column recompute + conv + chunk plan in one launch, then the chunked scan and the
+// gated norm + quant, in stream order.
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st);
 
 // SSD chunk kernels on the bf16 MFMA (ssd.hip): per (chunk, head) dt, cumulative
