@@ -1,6 +1,7 @@
 #!/usr/bin/env python3
 """Mixer throughput on one MI355X: paged decode B=8 through 23 stacked blocks (the
-headline line) and prefill of one 512-token sequence through one block.
+headline line), prefill of one 512-token sequence through one block, and one block of
+the ragged prefill (8192 + 4096 + 2048 + 1024 tokens).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
 
@@ -27,6 +28,7 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 WORKLOAD_DECODE = 2          # paged decode B=8, 23 blocks
 WORKLOAD_PREFILL = 3         # prefill 512, one block
+WORKLOAD_RAGGED = 4          # ragged prefill 8192 + 4096 + 2048 + 1024 tokens, zero initial state
 
 
 def log(msg):
@@ -300,6 +302,40 @@ def main():
         gemm_large[name] = {"us": round(us, 1), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
         del a, o
     log(f"GEMMs at m = {TL}: {gemm_large}")
+    # one block of the ragged prefill (4 sequences, 15,360 tokens, zero initial state), replayed
+    from workloads import RAGGED_LENGTHS
+    rp = block_params(WORKLOAD_RAGGED, 0)
+    rpar = nhm.MixerParams(nhm.Fp8Weight(up(rp["in_w"]), up(rp["in_w_scale"]), up(rp["in_a_scale"])),
+                           nhm.Fp8Weight(up(rp["out_w"]), up(rp["out_w_scale"]), up(rp["out_a_scale"])),
+                           up(rp["conv_w"]), up(rp["conv_b"]), up(rp["norm_w"]), up(rp["A_log"]), up(rp["D"]),
+                           up(rp["dt_bias"]))
+    rl = list(RAGGED_LENGTHS)
+    RT = int(sum(rl))
+    rh = up(hidden(WORKLOAD_RAGGED, RT))
+    rsp = torch.zeros((8, 64, 64, 128), dtype=torch.float32, device=dev)
+    rcp = torch.zeros((8, 3, 6144), dtype=torch.int16, device=dev)
+    rcu = up(np.concatenate([[0], np.cumsum(rl)]).astype(np.int32))
+    rsl = up(slots(WORKLOAD_RAGGED, len(rl), 8))
+    rhi = up(np.zeros(len(rl), np.int32))
+    rws = torch.zeros(nhm.prefill_ws_layout(RT, len(rl))["total"], dtype=torch.uint8, device=dev)
+    rout = torch.empty((RT, HIDDEN), dtype=torch.int16, device=dev)
+    rg = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(rg, stream=cap):
+        nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws)
+    for _ in range(2):
+        rg.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        rg.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    rag_us = e0.elapsed_time(e1) * 1e3 / 10
+    log(f"ragged prefill {rl}: {rag_us:.1f} us/block, {RT / (rag_us * 1e-6):.0f} tokens/s")
+    del rh, rws, rout, rsp, rcp
     gemm_us = gemm["in_proj"]["us"] + gemm["out_proj"]["us"]
     gemm_tflops = 2 * T * 38707200 / (gemm_us * 1e-6) / 1e12
     log(f"prefill 512: {pre_us:.1f} us/block, {T / (pre_us * 1e-6):.0f} tokens/s; GEMMs {gemm}")
@@ -330,6 +366,8 @@ def main():
                         "gemm": gemm, "gemm_bound": "mfma", "gemm_tflops": round(gemm_tflops, 1),
                         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
         "gemm_m15360": gemm_large,
+        "prefill_ragged_15360": {"lengths": rl, "us_per_block": round(rag_us, 1),
+                                 "tokens_per_s": round(RT / (rag_us * 1e-6), 1)},
         "parity_sample": parity,
         "cpu_baseline": cpu,
     }
