@@ -16,7 +16,7 @@ __all__ = ["lib", "LIB_PATH", "NhmError", "Geometry", "Layout", "WsLayout", "Fp8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnhm.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_w8a8_linear_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python fp8_w8a8_linear_amd/build.py` "
                       "(or __graft_entry__.build()); this package has no non-HIP fallback")
 lib = C.CDLL(LIB_PATH)
 

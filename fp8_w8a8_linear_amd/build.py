@@ -1,6 +1,6 @@
 """Build libnhm.so (gfx950) in-tree with hipcc.
 
-    python -m fp8_w8a8_linear_amd.build        # or fp8_w8a8_linear_amd.build.build()
+    python fp8_w8a8_linear_amd/build.py        # or __graft_entry__.build()
 
 Every translation unit is compiled each time (a few seconds each, in parallel).
 Packed-fp32 instruction selection is disabled for all device code.
