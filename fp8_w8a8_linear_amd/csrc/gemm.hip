@@ -16,7 +16,7 @@
 //    one XCD so the panel is fetched into that XCD's L2 once. Loads go through
 //    buffer descriptors, whose range check returns zeros past the operand's end,
 //    so ragged edges and padded steps need no branches in the loop.
-//  * 256 x 256 tile kernel (enough tiles to fill the chip): both operand tiles
+//  * 256 x 256 and 256 x 128 tile kernels (enough tiles to fill the chip): both operand tiles
 //    stream into a five-stage LDS ring by direct-to-LDS buffer loads (no register
 //    round trip; the range check zero-fills ragged rows and k), eight waves of
 //    128 x 64 on the 32x32x64 MFMA read the operands of the next stage while the
@@ -314,11 +314,20 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWT = 256;               // workgroup tile, n and m
+constexpr int kWT = 256;               // workgroup tile extent in n (and in m for the square tile)
 constexpr int kWK = 64;                // k bytes per ring stage (one 32x32x64 MFMA deep)
-constexpr int kRing = 5;               // ring stages: 5 x 32 KB fills the 160 KB LDS
-constexpr int kOpStage = kWT * kWK;    // one operand's stage, 16 KB
-constexpr int kStage = 2 * kOpStage;
+constexpr int kWStage = kWT * kWK;     // the weight tile's part of a stage, 16 KB
+
+// Ring geometry of a 256 (n) x TM (m) tile: a stage holds 256 weight rows then TM activation
+// rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for TM = 256, 6 x 24 KB
+// for TM = 128).
+template <int TM>
+struct RingShape {
+    static constexpr int kStage = (kWT + TM) * kWK;
+    static constexpr int kRing = (160 * 1024) / kStage;
+    static constexpr int kJX = TM / 128;          // 32-row activation blocks per wave (wave tile m = TM / 4)
+    static constexpr int kLoads = 2 + kJX;        // 16-row DMA instructions per wave per stage
+};
 
 __device__ __forceinline__ v16f mfma32_e4m3(const v8i& a, const v8i& b, const v16f& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -363,70 +372,80 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Operands under 2^31 bytes (buffer offsets). Grid = number of 256 x 256 tiles, 512 threads.
+// Operands under 2^31 bytes (buffer offsets). Grid = number of 256 x TM tiles, 512 threads.
+template <int TM>
 __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
+    using RS = RingShape<TM>;
+    constexpr int kStage = RS::kStage, kRing = RS::kRing, kJX = RS::kJX, kLoads = RS::kLoads;
+    static_assert(TM == 256 || TM == 128, "tile m extent");
+    static_assert(kRing >= 4 && (kRing - 2) * kLoads < 64, "ring depth and the vmcnt field");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
-    static_assert(kRing * kStage >= kWT * kWT * 2, "the epilogue stages the whole bf16 tile in the ring");
+    static_assert(kRing * kStage >= TM * kWT * 2, "the epilogue stages the whole bf16 tile in the ring");
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n 128 x m 64
+    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n 128 x m TM / 4
     const int r32 = lane & 31, q = lane >> 5;
 
     // Blocks go to the 8 XCDs round robin; each XCD takes a contiguous share of the tiles in an
     // order that walks 8 m-tiles per n-tile, so the ~32 tiles an XCD holds at once share 8
     // activation and 4 weight panels through its L2.
-    const int ntn = (int)((g.n + kWT - 1) / kWT), ntm = (int)((g.m + kWT - 1) / kWT);
+    const int ntn = (int)((g.n + kWT - 1) / kWT), ntm = (int)((g.m + TM - 1) / TM);
     const int total = ntn * ntm;
     const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
     const int j = x * (total >> 3) + min(x, total & 7) + loc;
     constexpr int kGroupM = 8;
     const int grp = j / (kGroupM * ntn), within = j - grp * kGroupM * ntn;
     const int gms = min(kGroupM, ntm - grp * kGroupM);
-    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * kWT, n0 = (int64_t)(within / gms) * kWT;
+    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * TM, n0 = (int64_t)(within / gms) * kWT;
 
-    // DMA: wave w fills rows 32 w .. 32 w + 31 of both operand tiles of a stage, 16 rows per
-    // instruction; lane l lands in slot l of the instruction's 1 KB: row 16 i + l / 4, chunk
-    // slot l % 4, which holds the logical chunk kc / 16 under the swizzle.
+    // DMA: wave w fills weight rows 32 w .. 32 w + 31 and activation rows (TM / 8) w ..
+    // (TM / 8) (w + 1) - 1 of a stage, 16 rows per instruction; lane l lands in slot l of the
+    // instruction's 1 KB: row 16 i + l / 4, chunk slot l % 4, which holds the logical chunk
+    // kc / 16 under the swizzle (the swizzle depends on the row modulo 16 only).
     const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
     const int lr = lane >> 2;
     const int kc = ((lane & 3) ^ (((lr >> 1) ^ (lr >> 2)) & 3)) * 16;
-    uint32_t wb[2], ab[2];
+    uint32_t wb[2], ab[kJX];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = wave * 32 + i * 16 + lr;
         wb[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < kJX; ++i) {
+        const int row = wave * (TM / 8) + i * 16 + lr;
         ab[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
     }
     auto issue = [&](int s) {   // stage s (s may run past k: its loads are out of range, zeros)
         const uint32_t k0 = (uint32_t)s * kWK;
         const bool kin = (int64_t)k0 + kc < g.k;
-        uint8_t* sb = smem + (s % kRing) * kStage + wave * 2048;
+        uint8_t* sb = smem + (s % kRing) * kStage;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            dma16(wrs, sb + i * 1024, kin ? wb[i] + k0 : kOutOfRange);
-            dma16(ars, sb + kOpStage + i * 1024, kin ? ab[i] + k0 : kOutOfRange);
-        }
+        for (int i = 0; i < 2; ++i) dma16(wrs, sb + (wave * 32 + i * 16) * kWK, kin ? wb[i] + k0 : kOutOfRange);
+#pragma unroll
+        for (int i = 0; i < kJX; ++i)
+            dma16(ars, sb + kWStage + (wave * (TM / 8) + i * 16) * kWK, kin ? ab[i] + k0 : kOutOfRange);
     };
-    auto read_ops = [&](int s, v8i (&wop)[4], v8i (&aop)[2]) {
+    auto read_ops = [&](int s, v8i (&wop)[4], v8i (&aop)[kJX]) {
         const uint8_t* sw = smem + (s % kRing) * kStage;
-        const uint8_t* sa = sw + kOpStage;
+        const uint8_t* sa = sw + kWStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = wn * 128 + i * 32 + r32;
             wop[i] = cat8(lds16(sw + swz64(row, 2 * q)), lds16(sw + swz64(row, 2 * q + 1)));
         }
 #pragma unroll
-        for (int jx = 0; jx < 2; ++jx) {
-            const int row = wm * 64 + jx * 32 + r32;
+        for (int jx = 0; jx < kJX; ++jx) {
+            const int row = wm * (TM / 4) + jx * 32 + r32;
             aop[jx] = cat8(lds16(sa + swz64(row, 2 * q)), lds16(sa + swz64(row, 2 * q + 1)));
         }
     };
 
-    v16f acc[4][2];
+    v16f acc[4][kJX];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jx = 0; jx < 2; ++jx)
+        for (int jx = 0; jx < kJX; ++jx)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
 
@@ -435,8 +454,8 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
     // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
     // stage kt (read one step earlier) run.
-    auto step = [&](int kt, const v8i (&cw)[4], const v8i (&ca)[2], v8i (&nw)[4], v8i (&na)[2]) {
-        wait_vmcnt<(kRing - 3) * 4>();
+    auto step = [&](int kt, const v8i (&cw)[4], const v8i (&ca)[kJX], v8i (&nw)[4], v8i (&na)[kJX]) {
+        wait_vmcnt<(kRing - 3) * kLoads>();
         __syncthreads();
         issue(kt + kRing - 1);
         if (kt + 1 < nk) read_ops(kt + 1, nw, na);
@@ -444,13 +463,13 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jx = 0; jx < 2; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
+            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
         __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
     };
 #pragma unroll
     for (int s = 0; s < kRing - 1; ++s) issue(s);
-    v8i w0[4], a0[2], w1[4], a1[2];
-    wait_vmcnt<(kRing - 2) * 4>();
+    v8i w0[4], a0[kJX], w1[4], a1[kJX];
+    wait_vmcnt<(kRing - 2) * kLoads>();
     __syncthreads();
     read_ops(0, w0, a0);
     int kt = 0;
@@ -478,8 +497,8 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
 #pragma unroll
-            for (int jx = 0; jx < 2; ++jx) {
-                const int ml = wm * 64 + jx * 32 + r32;
+            for (int jx = 0; jx < kJX; ++jx) {
+                const int ml = wm * (TM / 4) + jx * 32 + r32;
                 const int hs = ((ml >> 3) ^ (ml >> 4)) & 1;
                 *reinterpret_cast<uint2*>(smem + ml * 512 + (((nl >> 3) ^ (ml & 15)) << 4) + ((q ^ hs) << 3)) =
                     make_uint2(pk_bf16(acc[i][jx][4 * gq] * sc[0], acc[i][jx][4 * gq + 1] * sc[1]),
@@ -488,9 +507,9 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
         }
     __syncthreads();
     const bool vec = (g.ld_out & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
-    const bool full = vec && m0 + kWT <= g.m && n0 + kWT <= g.n;
+    const bool full = vec && m0 + TM <= g.m && n0 + kWT <= g.n;
 #pragma unroll 4
-    for (int it = 0; it < kWT * kWT / 8 / 512; ++it) {
+    for (int it = 0; it < TM * kWT / 8 / 512; ++it) {
         const int e = t + it * 512, ml = e >> 5, cn = e & 31;
         uint4 v = lds16(smem + ml * 512 + ((cn ^ (ml & 15)) << 4));
         if (((ml >> 3) ^ (ml >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
@@ -520,7 +539,9 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 }
 
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
-// panel kernel with 128 x 192 tiles takes in_proj from 37 to 33 us; where those
+// 256 x 128 ring kernel (164 tiles) takes in_proj to 28.8 us from the panel kernel's 30.4
+// (its deeper, register-free prefetch); the panel kernel with 128 x 192 tiles took it from
+// 37 to 33 us; where those
 // tiles give too few workgroups to fill the chip (out_proj: 56), 64 x 128 tiles
 // (168 workgroups) take it from 34 to 21 us. The 256 x 256 kernel leads from about
 // 160 of its tiles (m = 1024 for in_proj, m = 4096 for out_proj: 45 vs 54 us and
@@ -533,6 +554,11 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
                ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0};
     // buffer descriptors address the operands with 32-bit offsets
     const bool offsets_fit = n * k < (int64_t(1) << 31) && m * lda < (int64_t(1) << 31);
+    const int64_t half_tiles = ((n + kWT - 1) / kWT) * ((m + 127) / 128);
+    if (m <= 640 && offsets_fit && half_tiles >= 160) {
+        tile256_kernel<128><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
+        return check_launch("gemm (256 x 128)");
+    }
     if (m <= 640 && offsets_fit) {
         const int64_t big_tiles = ((n + 191) / 192) * ((m + 127) / 128);
         if (big_tiles >= 160)
@@ -543,7 +569,7 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
     }
     const int64_t wide_tiles = ((n + kWT - 1) / kWT) * ((m + kWT - 1) / kWT);
     if (offsets_fit && wide_tiles >= 160) {
-        tile256_kernel<<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
+        tile256_kernel<256><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 256)");
     }
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));

@@ -49,6 +49,52 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
            (e4m3_nan(d, r >> 24) << 24);
 }
 
+// The eight bf16 values of a 16-byte load, in memory order.
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = bf16_to_f32(w[j] & 0xffffu);
+        f[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+}
+
+// E4M3(x / s) for positive scales in [2^-80, 2^100], without a division per element.
+// With r = 1/s rounded to nearest (one IEEE division per thread), q0 = RN(x r) is corrected
+// once by the exact residual: q = RN(q0 - RN(q0 s - x) r). This equals the IEEE quotient
+// RN(x / s) bit for bit, signed zeros included: checked on the host's IEEE f32 arithmetic
+// (tests/c/recip_div_check.c) over every bf16 significand (both signs) against every f32
+// scale significand in [1, 2) (2^31 pairs; exponents only scale both sides inside this
+// range), and over all 65,536 bf16 patterns at scales spread over 2^-80 .. 2^99. The product is clamped to
+// +-2^100 so that the residual stays finite when x r overflows (such quotients saturate to
+// +-448 either way). NaN inputs take 0x7F with their own sign, as the IEEE quotient of a
+// NaN is that NaN. Other scales (negative, tiny, huge, NaN) use the IEEE division.
+__device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-80f && s <= 0x1p100f; }
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+    const float q0 = __builtin_amdgcn_fmed3f(x * r, -0x1p100f, 0x1p100f);
+    return fmaf(fmaf(q0, s, -x), -r, q0);
+}
+// Eight bf16 values (a 16-byte load, memory order) to eight e4m3 codes (8 bytes, memory
+// order) with the quotient of div_by_scale (fast_scale(s) must hold, r = 1/s). Finite
+// inputs only: where bf16x8_special() holds for any input of the wave, the caller takes
+// quant_bf16x8 instead (NaN codes), behind one wave-uniform branch.
+__device__ __forceinline__ uint2 quant_bf16x8_fast(const uint4 v, float s, float r) {
+    float x[8], q[8];
+    unpack8(v, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_fmed3f(div_by_scale(x[j], s, r), -448.0f, 448.0f);
+    uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)lo, true);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)hi, true);
+    return make_uint2(lo, hi);
+}
+// Non-zero when one of eight bf16 values has an exponent field of all ones (inf or NaN):
+// (h & 0x7f80) + 0x80 carries into the sign position of its half.
+__device__ __forceinline__ uint32_t bf16x8_special(const uint4 v) {
+    return (((v.x & 0x7f807f80u) + 0x00800080u) | ((v.y & 0x7f807f80u) + 0x00800080u) |
+            ((v.z & 0x7f807f80u) + 0x00800080u) | ((v.w & 0x7f807f80u) + 0x00800080u)) & 0x80008000u;
+}
 // Exact float value of an e4m3 code (finite codes; the GEMMs never decode in software).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
     const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
@@ -65,15 +111,9 @@ __device__ __forceinline__ uint32_t quant_bf16x4(uint32_t w0, uint32_t w1, float
     return e4m3x4(__fdiv_rn(bf16_to_f32(w0 & 0xffffu), s), __fdiv_rn(bf16_to_f32(w0 >> 16), s),
                   __fdiv_rn(bf16_to_f32(w1 & 0xffffu), s), __fdiv_rn(bf16_to_f32(w1 >> 16), s));
 }
-
-// The eight bf16 values of a 16-byte load, in memory order.
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f[2 * j] = bf16_to_f32(w[j] & 0xffffu);
-        f[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-    }
+// Eight bf16 values to eight codes as quant_bf16 (IEEE division; any scale).
+__device__ __forceinline__ uint2 quant_bf16x8(const uint4 v, float s) {
+    return make_uint2(quant_bf16x4(v.x, v.y, s), quant_bf16x4(v.z, v.w, s));
 }
 
 // x * sigmoid(x) with the hardware reciprocal (about 1 ulp) instead of an IEEE division

@@ -24,6 +24,8 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     const uint16_t* yr = a.y + tok * a.d_inner + (int64_t)g * gw;
     const uint16_t* zr = a.zxbcdt + tok * a.d_in_proj + a.z_off + (int64_t)g * gw;
     const float so = *a.out_a_scale;
+    const bool fast = fast_scale(so);    // the quant's reciprocal form (exact; see quant_bf16x8_fast)
+    const float rso = __fdiv_rn(1.0f, so);
     auto emit = [&](int c, const float (&v)[8], float r) {
         float w[8];
         unpack8(*reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c), w);
@@ -32,7 +34,11 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
         for (int j = 0; j < 4; ++j) ob[j] = f32x2_to_bf16x2(v[2 * j] * r * w[2 * j], v[2 * j + 1] * r * w[2 * j + 1]);
         const int64_t o = tok * a.d_inner + (int64_t)g * gw + c;
         if (a.norm) *reinterpret_cast<uint4*>(a.norm + o) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
-        *reinterpret_cast<uint2*>(a.q_out + o) = make_uint2(quant_bf16x4(ob[0], ob[1], so), quant_bf16x4(ob[2], ob[3], so));
+        const uint4 ov = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        uint2 code;
+        if (fast && __builtin_amdgcn_ballot_w64(bf16x8_special(ov) != 0u) == 0) code = quant_bf16x8_fast(ov, so, rso);
+        else code = quant_bf16x8(ov, so);
+        *reinterpret_cast<uint2*>(a.q_out + o) = code;
     };
     float ss = 0.f;
     if constexpr (kIt > 0) {

@@ -13,11 +13,17 @@ __global__ __launch_bounds__(256) void quant_vec8_kernel(const uint16_t* __restr
                                                         uint8_t* __restrict__ q, int64_t ld_q) {
     const float s = *scale;
     const int64_t total = rows * vec_per_row;
+    // the scale is uniform: one branch picks the reciprocal form or the IEEE division
+    const bool fast = fast_scale(s);
+    const float rs = __fdiv_rn(1.0f, s);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / vec_per_row, v = i - r * vec_per_row;
         const uint4 in = *reinterpret_cast<const uint4*>(x + r * ld_x + v * 8);
-        *reinterpret_cast<uint2*>(q + r * ld_q + v * 8) = make_uint2(quant_bf16x4(in.x, in.y, s), quant_bf16x4(in.z, in.w, s));
+        uint2 code;
+        if (fast && __builtin_amdgcn_ballot_w64(bf16x8_special(in) != 0u) == 0) code = quant_bf16x8_fast(in, s, rs);
+        else code = quant_bf16x8(in, s);
+        *reinterpret_cast<uint2*>(q + r * ld_q + v * 8) = code;
     }
 }
 

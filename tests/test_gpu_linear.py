@@ -66,9 +66,10 @@ def test_linear_sweep_shapes(nhm, m, n, k):
     _check(nhm, a, w, ws, sa)
 
 
-# m <= 16: GEMV; m <= 640: panel kernel (128 x 192 tiles when they give >= 160 workgroups,
-# else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160 tiles (the last two
-# shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
+# m <= 16: GEMV; m <= 640: the 256 x 128 ring kernel when it has >= 160 tiles (500 x 10000
+# x 2672: 160 tiles, ragged m, n and k), else the panel kernel (128 x 192 tiles when they give
+# >= 160 workgroups, else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160
+# tiles (the last two shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
 # x 272: partial m and n tiles, n % 8 != 0, k ending inside a 64-byte ring stage).
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
                                    (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
