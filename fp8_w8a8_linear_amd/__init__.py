@@ -12,7 +12,8 @@ import os
 
 __all__ = ["lib", "LIB_PATH", "NhmError", "Geometry", "Layout", "WsLayout", "Fp8Weight", "MixerParams",
            "GEOMETRY", "mixer_layout", "quantize_static", "fp8_linear", "fp8_linear_workspace_bytes",
-           "decode_ws_layout", "prefill_ws_layout", "mixer_decode", "mixer_prefill", "NHM_BF16", "NHM_E4M3"]
+           "decode_ws_layout", "prefill_ws_layout", "mixer_decode", "mixer_prefill", "NHM_BF16", "NHM_E4M3",
+           "NHM_F32"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnhm.so")
 if not os.path.exists(LIB_PATH):
@@ -20,7 +21,7 @@ if not os.path.exists(LIB_PATH):
                       "(or __graft_entry__.build()); this package has no non-HIP fallback")
 lib = C.CDLL(LIB_PATH)
 
-NHM_BF16, NHM_E4M3 = 0, 1
+NHM_BF16, NHM_E4M3, NHM_F32 = 0, 1, 2
 _STATUS = {0: "NHM_OK", 1: "NHM_ERR_NULL", 2: "NHM_ERR_SHAPE", 3: "NHM_ERR_ALIGN", 4: "NHM_ERR_UNSUPPORTED",
            5: "NHM_ERR_WORKSPACE", 6: "NHM_ERR_HIP"}
 
@@ -66,6 +67,7 @@ _SIGS = {
     "nhm_fp8_quantize_static": (C.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "nhm_fp8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int]),
     "nhm_fp8_linear": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, _i64, _p, _sz, _p]),
+    "nhm_fp8_linear_ex": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, C.c_int, _i64, _p, _sz, _p]),
     "nhm_mixer_decode_ws_layout": (C.c_int, [C.POINTER(Geometry), _i32, C.POINTER(WsLayout)]),
     "nhm_mixer_prefill_ws_layout": (C.c_int, [C.POINTER(Geometry), _i64, _i32, _i32, C.POINTER(WsLayout)]),
     "nhm_mixer_decode": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p]),
@@ -164,20 +166,24 @@ def fp8_linear_workspace_bytes(m, n, k, a_type):
     return int(lib.nhm_fp8_linear_workspace_bytes(m, n, k, a_type))
 
 
-def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None):
-    """bf16 [m, n] = W8A8(a [m, k], weight). a: bf16 bits (int16/uint16/bfloat16) or e4m3 codes (uint8)."""
+def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None, out_type=None):
+    """[m, n] = W8A8(a [m, k], weight). a: bf16 bits (int16/uint16/bfloat16) or e4m3 codes (uint8).
+
+    The output is bf16 bits (int16) unless out_type is NHM_F32 (or out is a float32 tensor)."""
     import torch
     a = _dev_tensor(a, "a")
     if a_type is None:
         a_type = NHM_E4M3 if a.dtype == torch.uint8 else NHM_BF16
+    if out_type is None:
+        out_type = NHM_F32 if out is not None and out.dtype == torch.float32 else NHM_BF16
     m = int(a.shape[0])
     if out is None:
-        out = torch.empty((m, weight.n), dtype=torch.int16, device=a.device)
+        out = torch.empty((m, weight.n), dtype=torch.float32 if out_type == NHM_F32 else torch.int16, device=a.device)
     need = fp8_linear_workspace_bytes(m, weight.n, weight.k, a_type)
     if ws is None and need > 0:
         ws = torch.zeros(need, dtype=torch.uint8, device=a.device)
-    _check(lib.nhm_fp8_linear(_ptr(a), a_type, m, a.shape[1], C.byref(weight.struct), _ptr(out), out.shape[1],
-                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    _check(lib.nhm_fp8_linear_ex(_ptr(a), a_type, m, a.shape[1], C.byref(weight.struct), _ptr(out), out_type,
+                                 out.shape[1], _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out
 
 

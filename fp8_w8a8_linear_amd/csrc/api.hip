@@ -134,12 +134,12 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
 // the GEMV, which carries the conv epilogue, and reports geometries beyond its limits.
 static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
 
-// One projection on an e4m3 activation [m, lda].
+// One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
-                          int64_t ld_out, const ConvEpilogue* conv, hipStream_t st) {
+                          int64_t ld_out, const ConvEpilogue* conv, hipStream_t st, float* out_f32 = nullptr) {
     if (conv || use_gemv(m, w.n, w.k))
-        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st);
-    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st);
+        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st, out_f32);
+    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
 }
 
 static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
@@ -210,7 +210,14 @@ size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype
 
 nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
                           uint16_t* out, int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+    return nhm_fp8_linear_ex(a, a_type, m, ld_a, w, out, NHM_BF16, ld_out, ws, ws_bytes, stream);
+}
+
+nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
+                             void* out, nhm_dtype out_type, int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    if (out_type != NHM_BF16 && out_type != NHM_F32)
+        return fail(NHM_ERR_UNSUPPORTED, "output dtype %d: bf16 or f32", (int)out_type);
     if (!w) return fail(NHM_ERR_NULL, "weight is NULL");
     if (a_type != NHM_BF16 && a_type != NHM_E4M3) return fail(NHM_ERR_UNSUPPORTED, "unknown activation dtype %d", (int)a_type);
     if (m < 0) return fail(NHM_ERR_SHAPE, "negative m");
@@ -226,7 +233,8 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
                     (long long)ld_out, (long long)w->n);
     if (!aligned(a, 16) || (a_type == NHM_BF16 ? ld_a % 8 : ld_a % 16) != 0)
         return fail(NHM_ERR_ALIGN, "a must be 16-byte aligned with 16-byte row stride");
-    if (!aligned(out, 2)) return fail(NHM_ERR_ALIGN, "out must be 2-byte aligned");
+    if (!aligned(out, out_type == NHM_F32 ? 4 : 2))
+        return fail(NHM_ERR_ALIGN, "out must be aligned to its element size");
     const size_t need = linear_ws(m, w->k, a_type);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
@@ -242,7 +250,8 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
         aq = q;
         lda = w->k;
     }
-    return project(aq, lda, m, *w, out, ld_out, nullptr, st);
+    if (out_type == NHM_F32) return project(aq, lda, m, *w, nullptr, ld_out, nullptr, st, static_cast<float*>(out));
+    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, nullptr, st);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {

@@ -33,7 +33,8 @@ namespace nhm {
 struct GemmArgs {
     const uint8_t* a; int64_t lda; int64_t m;
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
-    uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: 8-byte aligned rows
+    uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
+    float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
 };
 
 // Row r of a 128-byte-wide LDS tile holds its 16-byte chunk c at slot c ^ (r & 7):
@@ -60,6 +61,20 @@ __device__ __forceinline__ void store_tile(uint16_t* out, int64_t ld_out, int64_
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (nb + r < n) out[mm * ld_out + nb + r] = (uint16_t)hb[r];
+    }
+}
+
+// The same tile as f32 (acc * scale, no rounding); full: 16-byte aligned rows.
+__device__ __forceinline__ void store_tile_f32(float* out, int64_t ld_out, int64_t mm, int64_t nb, int64_t m, int64_t n,
+                                               const v4f& acc, const float (&sc)[4], bool full) {
+    const float4 v = make_float4(acc[0] * sc[0], acc[1] * sc[1], acc[2] * sc[2], acc[3] * sc[3]);
+    if (full) {
+        *reinterpret_cast<float4*>(out + mm * ld_out + nb) = v;
+    } else if (mm < m) {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (nb + r < n) out[mm * ld_out + nb + r] = e[r];
     }
 }
 
@@ -193,7 +208,10 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
         for (int r = 0; r < 4; ++r) sc[r] = sa * wsc[i][r];
 #pragma unroll
         for (int j = 0; j < TM; ++j)
-            store_tile(g.out, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, g.n, acc[i][j], sc, full);
+            if (g.out_f32)
+                store_tile_f32(g.out_f32, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, g.n, acc[i][j], sc, full);
+            else
+                store_tile(g.out, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, g.n, acc[i][j], sc, full);
     }
 }
 
@@ -302,8 +320,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
         for (int r = 0; r < 4; ++r) sc[r] = sa * wsc[i][r];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            store_tile(g.out, g.ld_out, m0 + wm * 64 + j * 16 + r16, n0 + wn * 64 + i * 16 + 4 * q, g.m, g.n, acc[i][j],
-                       sc, full);
+            if (g.out_f32)
+                store_tile_f32(g.out_f32, g.ld_out, m0 + wm * 64 + j * 16 + r16, n0 + wn * 64 + i * 16 + 4 * q, g.m, g.n,
+                               acc[i][j], sc, full);
+            else
+                store_tile(g.out, g.ld_out, m0 + wm * 64 + j * 16 + r16, n0 + wn * 64 + i * 16 + 4 * q, g.m, g.n,
+                           acc[i][j], sc, full);
     }
 }
 
@@ -485,8 +507,28 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     // 16-byte chunk cn of row ml at slot cn ^ (ml & 15) with its two 8-byte halves swapped when
     // bit 3 xor bit 4 of ml is set: the 8-byte writes of 32 rows at one n land in 32 distinct
     // slots of the 256-byte bank window. Each half-wave then stores one whole 512-byte row.
-    __syncthreads();   // every wave is done reading the ring
     const float sa = *g.a_scale;
+    if (g.out_f32) {
+        // f32 output: each lane stores its four consecutive n of one m row straight from the
+        // accumulators (16 bytes per lane; the output is twice the bf16 size, no LDS staging)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int64_t nb = n0 + wn * 128 + i * 32 + gq * 8 + q * 4;
+                float sc[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
+#pragma unroll
+                for (int jx = 0; jx < kJX; ++jx) {
+                    const int64_t mm = m0 + wm * (TM / 4) + jx * 32 + r32;
+                    const v4f a4 = {acc[i][jx][4 * gq], acc[i][jx][4 * gq + 1], acc[i][jx][4 * gq + 2], acc[i][jx][4 * gq + 3]};
+                    store_tile_f32(g.out_f32, g.ld_out, mm, nb, g.m, g.n, a4, sc, g.vec_out && mm < g.m && nb + 3 < g.n);
+                }
+            }
+        return;
+    }
+    __syncthreads();   // every wave is done reading the ring
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -549,9 +591,11 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 // (123 tiles at m = 641: 43 vs 36 us).
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st) {
+                       hipStream_t st, float* out_f32) {
     GemmArgs g{a, lda, m, w, w_scale, a_scale, n, k, out, ld_out,
-               ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0};
+               out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
+                       : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0,
+               out_f32};
     // buffer descriptors address the operands with 32-bit offsets
     const bool offsets_fit = n * k < (int64_t(1) << 31) && m * lda < (int64_t(1) << 31);
     const int64_t half_tiles = ((n + kWT - 1) / kWT) * ((m + 127) / 128);

@@ -22,7 +22,8 @@ constexpr int kGemvMaxSteps = 8;       // k-steps per wave held in registers
 struct GemvArgs {
     const uint8_t* a; int64_t lda; int m;
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
-    uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: 8-byte aligned rows
+    uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
+    float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
     int ksteps;
     ConvEpilogue conv;
 };
@@ -110,6 +111,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
     // acc[r] = D[feature nbase + r][token col]
     if (col >= g.m) return;
+    if (g.out_f32) {   // (never with the conv epilogue)
+        float* of = g.out_f32 + (int64_t)col * g.ld_out + nbase;
+        if (g.vec_out && nbase + 3 < g.n) {
+            *reinterpret_cast<float4*>(of) = make_float4(acc[0] * sc[0], acc[1] * sc[1], acc[2] * sc[2], acc[3] * sc[3]);
+        } else {
+            for (int r = 0; r < 4; ++r)
+                if (nbase + r < g.n) of[r] = acc[r] * sc[r];
+        }
+        return;
+    }
     uint32_t hb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[r] * sc[r]);
@@ -156,12 +167,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, hipStream_t st) {
+                       const ConvEpilogue* conv, hipStream_t st, float* out_f32) {
     GemvArgs g;
     g.a = a; g.lda = lda; g.m = m;
     g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
     g.out = out; g.ld_out = ld_out;
-    g.vec_out = ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+    g.out_f32 = conv ? nullptr : out_f32;
+    g.vec_out = out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
+                        : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
     g.ksteps = (int)((k + 127) / 128);
     g.conv = conv ? *conv : ConvEpilogue{};
     if (g.ksteps > 16 * kGemvMaxSteps)

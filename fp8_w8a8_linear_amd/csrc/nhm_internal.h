@@ -38,15 +38,16 @@ struct ConvEpilogue {
 
 // out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda].
 // conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue
-// (which needs the xBC range to start on a multiple of 32 features).
+// (which needs the xBC range to start on a multiple of 32 features). out_f32 (without
+// conv): the unrounded f32 result goes to out_f32[m * ld_out + n] instead of out.
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, hipStream_t st);
+                       const ConvEpilogue* conv, hipStream_t st, float* out_f32 = nullptr);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st);
+                       hipStream_t st, float* out_f32 = nullptr);
 
 // ---- decode SSM state update (decode.hip)
 struct DecodeSsmArgs {

@@ -63,7 +63,8 @@ typedef enum nhm_status {
 
 typedef enum nhm_dtype {
     NHM_BF16 = 0,            /* bfloat16 bit patterns (uint16_t)                   */
-    NHM_E4M3 = 1             /* OCP FP8 E4M3FN codes (uint8_t)                      */
+    NHM_E4M3 = 1,            /* OCP FP8 E4M3FN codes (uint8_t)                      */
+    NHM_F32 = 2              /* IEEE binary32 (float); an output type only          */
 } nhm_dtype;
 
 /* Static name of a status code. Never NULL. */
@@ -171,6 +172,20 @@ NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, n
 NHM_API nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
                           const nhm_fp8_weight* w, uint16_t* out, int64_t ld_out,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* nhm_fp8_linear with a choice of output type: out_type NHM_BF16 is nhm_fp8_linear;
+ * NHM_F32 stores the unrounded f32 result (sum_k val(a_q[i, k]) * val(w[j, k])) * a_scale
+ * * w_scale[j] instead of its bf16 rounding. [PR988] "The Thor finding, measured": the
+ * pages' fp8 GEMM plan takes the output dtype as part of its key, and both D = bf16 and
+ * D = f32 plans are probed available for the same six shapes.
+ *   out    (device) [m, ld_out] of out_type, ld_out >= n, aligned to its element size;
+ *          must not overlap a (16-byte aligned rows with ld_out % 4 == 0 are stored four
+ *          features at a time)
+ * Every other argument, the accumulation and the errors are those of nhm_fp8_linear;
+ * an out_type other than NHM_BF16 or NHM_F32 is NHM_ERR_UNSUPPORTED. */
+NHM_API nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
+                             const nhm_fp8_weight* w, void* out, nhm_dtype out_type, int64_t ld_out,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- the mixer block */
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(nhm):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(nhm.lib, n), f"{n} not exported"
 
@@ -73,6 +73,25 @@ def test_linear_refusals(nhm):
         st = _lin(nhm, kw["a"], kw["a_type"], kw["m"], kw["lda"], kw["w"], kw["out"], kw["ld_out"], kw["ws"], kw["wsb"])
         assert st == status, (over, st, nhm.lib.nhm_last_error())
         assert nhm.lib.nhm_last_error() != b""
+
+
+def test_linear_ex_refusals(nhm):
+    """The output-type variant: its own checks (type, f32 alignment), then nhm_fp8_linear's."""
+    A, O, WS = 0x10000, 0x20000, 0x40000
+    need = nhm.fp8_linear_workspace_bytes(32, 64, 128, nhm.NHM_BF16)
+    ex = nhm.lib.nhm_fp8_linear_ex
+    w = _w(nhm)
+    ok = dict(a=A, a_type=nhm.NHM_BF16, m=32, lda=128, out=O, out_type=nhm.NHM_F32, ld_out=64, ws=WS, wsb=need)
+    cases = [(dict(out_type=nhm.NHM_E4M3), 4), (dict(out_type=9), 4), (dict(out=O + 2), 3), (dict(out=None), 1),
+             (dict(ld_out=10), 2), (dict(a_type=7), 4), (dict(wsb=need - 1), 5)]
+    for over, status in cases:
+        kw = dict(ok)
+        kw.update(over)
+        st = ex(kw["a"], kw["a_type"], kw["m"], kw["lda"], C.byref(w), kw["out"], kw["out_type"], kw["ld_out"], kw["ws"],
+                kw["wsb"], None)
+        assert st == status, (over, st, nhm.lib.nhm_last_error())
+    # a bf16 output only needs 2-byte alignment, as in nhm_fp8_linear
+    assert ex(A, nhm.NHM_BF16, 0, 128, C.byref(w), O + 2, nhm.NHM_BF16, 64, WS, need, None) == 0
 
 
 def test_linear_zero_rows_is_noop(nhm):

@@ -68,12 +68,12 @@ def test_linear_sweep_shapes(nhm, m, n, k):
 
 # m <= 16: GEMV; m <= 640: the 256 x 128 ring kernel when it has >= 160 tiles (500 x 10000
 # x 2672: 160 tiles, ragged m, n and k), else the panel kernel (128 x 192 tiles when they give
-# >= 160 workgroups, else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160
+# >= 160 workgroups -- 384 x 10300 x 2608 -- else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160
 # tiles (the last two shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
 # x 272: partial m and n tiles, n % 8 != 0, k ending inside a 64-byte ring stage).
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
                                    (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
-                                   (500, 10000, 2672), (641, 130, 256), (700, 520, 272),
+                                   (384, 10300, 2608), (500, 10000, 2672), (641, 130, 256), (700, 520, 272),
                                    (2600, 4100, 272), (1030, 10304, 2688)])
 def test_linear_ragged(nhm, m, n, k):
     from workloads import linear_case
@@ -112,6 +112,62 @@ def test_linear_strided_output_wide_tiles(nhm, ld_pad):
     from workloads import linear_case
     a, w, ws, sa = linear_case(2600, 4100, 272, extra=6)
     _check(nhm, a, w, ws, sa, ld_pad=ld_pad)
+
+
+# f32 output (the D = f32 plan): the unrounded result, through every dispatch path -- GEMV
+# (m <= 16), the 256 x 128 ring tile (500 x 10000), the panel kernel (384 and 200 x 10304,
+# 130 x 70), the
+# 128 x 128 tile (641 x 130, 1030 x 2688) and the 256 x 256 tile (2600 x 4100 x 272, ragged).
+# Bound: the f32 accumulation term of the bf16 test without the bf16 rounding,
+# |gpu - ref| <= 2^-22 |ref| + 2^-16 * S.
+@pytest.mark.parametrize("m,n,k,via_e4m3,ld_pad", [(1, 10304, 2688, False, 0), (8, 2688, 4096, True, 0),
+                                                   (13, 100, 48, False, 5), (200, 10304, 2688, False, 0),
+                                                   (384, 10300, 2608, False, 0),
+                                                   (130, 70, 144, False, 0), (500, 10000, 2672, False, 0),
+                                                   (512, 2688, 4096, False, 0), (641, 130, 256, True, 0),
+                                                   (1030, 2688, 4096, False, 4), (2600, 4100, 272, False, 0),
+                                                   (2600, 4100, 272, False, 3)])
+def test_linear_f32_output(nhm, m, n, k, via_e4m3, ld_pad):
+    import ctypes as C
+    from oracle import e4m3_decode, fp8_linear, quantize_static
+    from tests.gpu_util import dev
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=8)
+    q = quantize_static(a, sa)
+    ref = fp8_linear(q, w, ws, sa)
+    S = np.abs(e4m3_decode(q)) @ np.abs(e4m3_decode(w)).T * np.float64(sa[0]) * ws.astype(np.float64)[None, :]
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    a_in, a_type = (dev(q), nhm.NHM_E4M3) if via_e4m3 else (dev(a), nhm.NHM_BF16)
+    out = torch.full((m, n + ld_pad), 12345.0, dtype=torch.float32, device="cuda")
+    need = nhm.fp8_linear_workspace_bytes(m, n, k, a_type)
+    wsb = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    st = nhm.lib.nhm_fp8_linear_ex(C.c_void_p(a_in.data_ptr()), a_type, m, k, C.byref(W.struct),
+                                   C.c_void_p(out.data_ptr()), nhm.NHM_F32, n + ld_pad, C.c_void_p(wsb.data_ptr()),
+                                   wsb.numel(), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, nhm.lib.nhm_last_error()
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == 12345.0)                       # the row padding is untouched
+    got = o[:, :n].astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -22 * np.abs(ref) + 2.0 ** -16 * S
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), f"at {worst}: got {got[worst]} ref {ref[worst]} bound {bound[worst]}"
+
+
+def test_linear_f32_output_binding(nhm):
+    """The binding's float32 output and the bf16 output agree up to the bf16 rounding."""
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(8, 10304, 2688, extra=9)
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    ad = dev(a)
+    of = nhm.fp8_linear(ad, W, out_type=nhm.NHM_F32)
+    ob = host(nhm.fp8_linear(ad, W))
+    torch.cuda.synchronize()
+    assert of.dtype == torch.float32
+    rounded = of.to(torch.bfloat16).view(torch.int16).cpu().numpy()
+    assert np.array_equal(rounded, ob.view(np.int16))
 
 
 @pytest.mark.parametrize("m", [8, 200, 512, 700, 4096])
