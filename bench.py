@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Mixer throughput on one MI355X: paged decode B=8 through 23 stacked blocks (the
-headline line), prefill of one 512-token sequence through one block, and one block of
-the ragged prefill (8192 + 4096 + 2048 + 1024 tokens).
+headline line), the same step on bf16 state pools (decode_bf16_state), prefill of one
+512-token sequence through one block, and one block of the ragged prefill (8192 + 4096 +
+2048 + 1024 tokens).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
 
@@ -35,14 +36,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_bytes_per_layer(B):
+def decode_bytes_per_layer(B, state_bytes=4):
     """Algorithmic HBM bytes of one decode call: weights + scales + small params once,
-    and per sequence the f32 state row read+write, the conv window read+write and the
-    bf16 block input and output."""
+    and per sequence the state row read+write (f32, or bf16 with state_bytes=2), the conv
+    window read+write and the bf16 block input and output."""
     w = 10304 * 2688 + 2688 * 4096
     scales = 4 * (10304 + 2688 + 2)
     small = 6144 * 4 * 2 + 6144 * 2 + 4096 * 2 + 3 * 64 * 4
-    per_seq = 2 * 64 * 64 * 128 * 4 + 2 * 3 * 6144 * 2 + 2 * 2688 * 2 + 4
+    per_seq = 2 * 64 * 64 * 128 * state_bytes + 2 * 3 * 6144 * 2 + 2 * 2688 * 2 + 4
     return w + scales + small + B * per_seq
 
 
@@ -233,6 +234,40 @@ def main():
     achieved = gb / (gemv_us * 1e-6) / 1e9
     log(f"in_proj GEMV m=8: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s")
 
+    # ------------------------------------------------------------ decode with a bf16 state pool
+    # the same step on bf16 copies of the state pools (rows widened to f32 in the kernel and
+    # rounded back on store): half the state bytes
+    spools16 = [sp.to(torch.bfloat16).view(torch.int16) for sp in spools]
+    torch.cuda.synchronize()
+
+    def step16(stream=None):
+        for l in range(N_LAYERS):
+            nhm.mixer_decode(params[l], acts[l], sl, spools16[l], cpools[l], acts[l + 1], ws, stream=stream)
+
+    with torch.cuda.stream(cap):
+        step16()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graph16 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph16, stream=cap):
+        step16()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph16.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        graph16.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms16 = e0.elapsed_time(e1) / args.steps
+    bytes16 = N_LAYERS * decode_bytes_per_layer(BATCH, state_bytes=2)
+    dec16 = {"us_per_step": round(ms16 * 1e3, 1), "tokens_per_s": round(BATCH / (ms16 * 1e-3), 1), "bytes": bytes16,
+             "achieved_GBs": round(bytes16 / (ms16 * 1e-3) / 1e9, 1),
+             "frac": round(bytes16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"decode step, bf16 state pools: {dec16}")
+    del spools16, graph16
+
     # ------------------------------------------------------------ prefill 512, one block
     pp = block_params(WORKLOAD_PREFILL, 0)
     ppar = nhm.MixerParams(nhm.Fp8Weight(up(pp["in_w"]), up(pp["in_w_scale"]), up(pp["in_a_scale"])),
@@ -358,6 +393,7 @@ def main():
                    "global_batch": BATCH, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "decode_step_hbm": {"bytes": step_bytes, "achieved_GBs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                             "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_bf16_state": dec16,
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel (in_proj 10304x2688, m=8)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),

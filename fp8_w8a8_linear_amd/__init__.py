@@ -73,6 +73,10 @@ _SIGS = {
     "nhm_mixer_decode": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p]),
     "nhm_mixer_prefill": (C.c_int, [C.POINTER(_MixerParams), _p, _i64, _p, _i32, _p, _p, _i32, _p, _p, _i32, _p,
                                     _p, _sz, _p]),
+    "nhm_mixer_decode_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p, _sz,
+                                      _p]),
+    "nhm_mixer_prefill_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i64, _p, _i32, _p, _p, _i32, _p, C.c_int, _p,
+                                       _i32, _p, _p, _sz, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -199,21 +203,34 @@ def prefill_ws_layout(n_tokens, n_seqs, chunk=128, g=GEOMETRY):
     return {n: int(getattr(out, n)) for n, _ in WsLayout._fields_}
 
 
+def _ssm_type(pool):
+    """NHM_F32 for a float32 state pool, NHM_BF16 for bf16 bits (int16/uint16) or bfloat16."""
+    import torch
+    if pool.dtype == torch.float32:
+        return NHM_F32
+    if pool.dtype in (torch.int16, torch.uint16, torch.bfloat16):
+        return NHM_BF16
+    raise TypeError(f"SSM state pool of dtype {pool.dtype}: float32 or bf16 bits")
+
+
 def mixer_decode(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out, ws, stream=None):
-    """One decode token per sequence; pools updated in place. ws: uint8 device tensor of the layout size."""
+    """One decode token per sequence; pools updated in place (f32 or bf16 state pool).
+    ws: uint8 device tensor of the layout size."""
     batch = int(hidden.shape[0])
-    _check(lib.nhm_mixer_decode(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
-                                _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws), ws.numel(),
-                                _stream(stream)))
+    _check(lib.nhm_mixer_decode_ex(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
+                                   _ssm_type(ssm_pool), _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
     return out
 
 
 def mixer_prefill(params: MixerParams, hidden, cu_seqlens, slot_idx, has_initial, ssm_pool, conv_pool, out, ws,
                   chunk=128, stream=None):
-    """Varlen prefill of packed sequences; pools updated in place. ws: uint8 device tensor of the layout size."""
+    """Varlen prefill of packed sequences; pools updated in place (f32 or bf16 state pool).
+    ws: uint8 device tensor of the layout size."""
     n_tokens = int(hidden.shape[0])
     n_seqs = int(slot_idx.shape[0])
-    _check(lib.nhm_mixer_prefill(C.byref(params.struct), _ptr(hidden), n_tokens, _ptr(cu_seqlens), n_seqs,
-                                 _ptr(slot_idx), _ptr(has_initial), chunk, _ptr(ssm_pool), _ptr(conv_pool),
-                                 int(ssm_pool.shape[0]), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    _check(lib.nhm_mixer_prefill_ex(C.byref(params.struct), _ptr(hidden), n_tokens, _ptr(cu_seqlens), n_seqs,
+                                    _ptr(slot_idx), _ptr(has_initial), chunk, _ptr(ssm_pool), _ssm_type(ssm_pool),
+                                    _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
     return out

@@ -280,7 +280,16 @@ nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_tokens, 
 nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch, const int32_t* slot_idx,
                             float* ssm_pool, uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws,
                             size_t ws_bytes, void* stream) {
+    return nhm_mixer_decode_ex(p, hidden, batch, slot_idx, ssm_pool, NHM_F32, conv_pool, n_slots, out, ws, ws_bytes,
+                               stream);
+}
+
+nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                               const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
+                               int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    if (ssm_type != NHM_F32 && ssm_type != NHM_BF16)
+        return fail(NHM_ERR_UNSUPPORTED, "SSM state dtype %d: f32 or bf16", (int)ssm_type);
     nhm_layout l;
     nhm_status s = check_params(p, &l);
     if (s != NHM_OK) return s;
@@ -314,7 +323,8 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
     }
     DecodeSsmArgs da;
     da.slot_idx = slot_idx;
-    da.ssm_pool = ssm_pool;
+    da.ssm_pool = ssm_type == NHM_F32 ? static_cast<float*>(ssm_pool) : nullptr;
+    da.ssm_pool_bf16 = ssm_type == NHM_BF16 ? static_cast<uint16_t*>(ssm_pool) : nullptr;
     da.zxbcdt = zx;
     da.xbc_conv = xc;
     da.A_log = p->A_log;
@@ -345,7 +355,18 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
                              const int32_t* cu_seqlens, int32_t n_seqs, const int32_t* slot_idx,
                              const int32_t* has_initial, int32_t chunk, float* ssm_pool, uint16_t* conv_pool,
                              int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    return nhm_mixer_prefill_ex(p, hidden, n_tokens, cu_seqlens, n_seqs, slot_idx, has_initial, chunk, ssm_pool,
+                                NHM_F32, conv_pool, n_slots, out, ws, ws_bytes, stream);
+}
+
+nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,
+                                const int32_t* cu_seqlens, int32_t n_seqs, const int32_t* slot_idx,
+                                const int32_t* has_initial, int32_t chunk, void* ssm_pool, nhm_dtype ssm_type,
+                                uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes,
+                                void* stream) {
     g_err[0] = 0;
+    if (ssm_type != NHM_F32 && ssm_type != NHM_BF16)
+        return fail(NHM_ERR_UNSUPPORTED, "SSM state dtype %d: f32 or bf16", (int)ssm_type);
     nhm_layout l;
     nhm_status s = check_params(p, &l);
     if (s != NHM_OK) return s;
@@ -409,7 +430,8 @@ nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, 
     a.cu_seqlens = cu_seqlens;
     a.slot_idx = slot_idx;
     a.has_initial = has_initial;
-    a.ssm_pool = ssm_pool;
+    a.ssm_pool = ssm_type == NHM_F32 ? static_cast<float*>(ssm_pool) : nullptr;
+    a.ssm_pool_bf16 = ssm_type == NHM_BF16 ? static_cast<uint16_t*>(ssm_pool) : nullptr;
     a.conv_pool = conv_pool;
     a.conv_w = p->conv_w;
     a.conv_b = p->conv_b;

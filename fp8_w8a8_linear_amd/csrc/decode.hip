@@ -11,7 +11,13 @@
 namespace nhm {
 
 constexpr int kP = 64, kN = 128;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // four bf16 state values
 
+// kBf16: the pool holds bf16 state (the cache dtype of a checkpoint whose SSM cache is not
+// f32): each row is widened to f32 on load (exact), advanced and read out in f32, and
+// rounded to bf16 (nearest even) on store -- the f32 working row of the f32 pool, narrowed
+// back to the cache dtype at the end of the step.
+template <bool kBf16>
 __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) {
     const int b = blockIdx.x, h = blockIdx.y;
     const int t = threadIdx.x;
@@ -26,10 +32,19 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
         return;
     }
     // element e = 4 * (t + 256 i): p = t / 32 + 8 i, n = 4 * (t % 32) .. + 3
-    v4f* st = reinterpret_cast<v4f*>(a.ssm_pool + (((int64_t)slot * a.n_heads + h) * kP) * kN);
+    const int64_t row0 = (((int64_t)slot * a.n_heads + h) * kP) * kN;
+    v4f* st = reinterpret_cast<v4f*>(a.ssm_pool + (kBf16 ? 0 : row0));
+    v2u* st16 = reinterpret_cast<v2u*>(a.ssm_pool_bf16 + (kBf16 ? row0 : 0));
     v4f hv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hv[i] = __builtin_nontemporal_load(st + t + 256 * i);
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (kBf16) {
+            const v2u u = __builtin_nontemporal_load(st16 + t + 256 * i);
+            hv[i] = v4f{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xffffu), bf16_to_f32(u[1] >> 16)};
+        } else {
+            hv[i] = __builtin_nontemporal_load(st + t + 256 * i);
+        }
+    }
 
     const uint16_t* xr = a.xbc_conv + (int64_t)b * a.conv_dim;
     if (t < kP) sx[t] = bf16_to_f32(xr[h * kP + t]);
@@ -52,7 +67,10 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
         v[1] = fmaf(dA, v[1], u * b1);
         v[2] = fmaf(dA, v[2], u * b2);
         v[3] = fmaf(dA, v[3], u * b3);
-        __builtin_nontemporal_store(v, st + t + 256 * i);
+        if constexpr (kBf16)
+            __builtin_nontemporal_store(v2u{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])}, st16 + t + 256 * i);
+        else
+            __builtin_nontemporal_store(v, st + t + 256 * i);
         yp[i] = v[0] * c0 + v[1] * c1 + v[2] * c2 + v[3] * c3;
     }
     // reduce over the 32 lanes that share p
@@ -72,7 +90,10 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
 }
 
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st) {
-    decode_ssm_kernel<<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
+    if (a.ssm_pool_bf16)
+        decode_ssm_kernel<true><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
+    else
+        decode_ssm_kernel<false><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
     return check_launch("decode_ssm");
 }
 

@@ -52,7 +52,8 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
 // ---- decode SSM state update (decode.hip)
 struct DecodeSsmArgs {
     const int32_t* slot_idx;
-    float* ssm_pool;
+    float* ssm_pool;           // f32 state pool, or nullptr with ssm_pool_bf16
+    uint16_t* ssm_pool_bf16;   // bf16 state pool (widened on load, rounded on store), or nullptr
     const uint16_t* zxbcdt;    // [m, d_in_proj]
     const uint16_t* xbc_conv;  // [m, conv_dim]
     const float* A_log;
@@ -86,7 +87,8 @@ struct PrefillArgs {
     const int32_t* cu_seqlens;
     const int32_t* slot_idx;
     const int32_t* has_initial;
-    float* ssm_pool;
+    float* ssm_pool;           // f32 state pool, or nullptr with ssm_pool_bf16
+    uint16_t* ssm_pool_bf16;   // bf16 state pool (widened on load, rounded on store), or nullptr
     uint16_t* conv_pool;
     const uint16_t* conv_w;
     const uint16_t* conv_b;

@@ -253,6 +253,9 @@ __device__ __forceinline__ void store_window(const PrefillArgs& a, int i, int c8
 // final state in the pool row (read first, written last by this workgroup only).
 // The first workgroups of each sequence also store its carried conv window (the conv
 // kernel, which reads the old window, has finished by now).
+// kBf16: a bf16 state pool, widened on the first read and rounded (nearest even) on the
+// final write; the pass itself runs in f32.
+template <bool kBf16>
 __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
     const int i = blockIdx.x, h = blockIdx.y, pb = blockIdx.z, t = threadIdx.x;
     {
@@ -261,8 +264,19 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
     }
     const int c0 = min(a.seq_chunk0[i], a.max_chunks), c1 = min(a.seq_chunk0[i + 1], a.max_chunks);
     const int64_t off = (int64_t)pb * 8 * kDS + 4 * t;
-    float4* pool = reinterpret_cast<float4*>(a.ssm_pool + ((int64_t)a.slot_idx[i] * a.n_heads + h) * kHP * kDS + off);
-    float4 H = a.has_initial[i] ? *pool : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t prow = ((int64_t)a.slot_idx[i] * a.n_heads + h) * kHP * kDS + off;
+    float4* pool = reinterpret_cast<float4*>(a.ssm_pool + (kBf16 ? 0 : prow));
+    uint2* pool16 = reinterpret_cast<uint2*>(a.ssm_pool_bf16 + (kBf16 ? prow : 0));
+    float4 H = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.has_initial[i]) {
+        if constexpr (kBf16) {
+            const uint2 u = *pool16;
+            H = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                            bf16_to_f32(u.y >> 16));
+        } else {
+            H = *pool;
+        }
+    }
     const int64_t hstride = (int64_t)kHP * kDS;
     float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c0 < c1) S = *reinterpret_cast<const float4*>(a.chunk_state + ((int64_t)c0 * a.n_heads + h) * hstride + off);
@@ -279,7 +293,10 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
         H.w = fmaf(dec, H.w, S.w);
         S = Snext;
     }
-    *pool = H;
+    if constexpr (kBf16)
+        *pool16 = make_uint2(f32x2_to_bf16x2(H.x, H.y), f32x2_to_bf16x2(H.z, H.w));
+    else
+        *pool = H;
 }
 
 // ---------------------------------------------------------------- launcher
@@ -290,7 +307,12 @@ nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     const int64_t n_exact = a.exact ? ((a.T + 15) / 16) * ((a.n_heads + 15) / 16) : 0;
     conv_fwd_kernel<<<dim3((unsigned)(n_exact + 1 + c8_blocks * tblocks)), 256, 0, st>>>(a, (int)n_exact, c8_blocks);
     if (a.max_chunks > 0) launch_ssd_state(a, st);
-    if (a.n_seqs > 0) ssd_pass_kernel<<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
+    if (a.n_seqs > 0) {
+        if (a.ssm_pool_bf16)
+            ssd_pass_kernel<true><<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
+        else
+            ssd_pass_kernel<false><<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
+    }
     if (a.max_chunks > 0) launch_ssd_out(a, st);
     nhm_status s = check_launch("prefill");
     if (s != NHM_OK || a.T == 0) return s;

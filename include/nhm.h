@@ -64,7 +64,7 @@ typedef enum nhm_status {
 typedef enum nhm_dtype {
     NHM_BF16 = 0,            /* bfloat16 bit patterns (uint16_t)                   */
     NHM_E4M3 = 1,            /* OCP FP8 E4M3FN codes (uint8_t)                      */
-    NHM_F32 = 2              /* IEEE binary32 (float); an output type only          */
+    NHM_F32 = 2              /* IEEE binary32 (float): GEMM output, SSM state       */
 } nhm_dtype;
 
 /* Static name of a status code. Never NULL. */
@@ -279,6 +279,26 @@ NHM_API nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* 
                              const int32_t* has_initial, int32_t chunk, float* ssm_pool,
                              uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* nhm_mixer_decode and nhm_mixer_prefill with a choice of SSM state dtype. ssm_type
+ * NHM_F32 is the calls above. NHM_BF16: ssm_pool is bf16 [n_slots, n_heads, head_dim,
+ * d_state] (the state of a checkpoint whose SSM cache dtype is not f32). [PR1288] "What it
+ * does": the gather widens the stored rows into an f32 working buffer and the result is
+ * narrowed back to the cache dtype, a different computation from the f32 pool (the two
+ * round differently). Here each touched row is widened to f32 when read (exact), the
+ * call runs exactly as with the f32 pool (outputs come from the f32 state), and the
+ * final state is rounded to bf16 (nearest even) when written back. The conv pool,
+ * every other argument and the errors are those of the calls above; an ssm_type other
+ * than NHM_F32 or NHM_BF16 is NHM_ERR_UNSUPPORTED. */
+NHM_API nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                               const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type,
+                               uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* ws,
+                               size_t ws_bytes, void* stream);
+NHM_API nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,
+                                const int32_t* cu_seqlens, int32_t n_seqs, const int32_t* slot_idx,
+                                const int32_t* has_initial, int32_t chunk, void* ssm_pool,
+                                nhm_dtype ssm_type, uint16_t* conv_pool, int32_t n_slots, uint16_t* out,
+                                void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,6 +52,7 @@ __all__ = [
     "quantize_static", "fp8_linear", "causal_conv1d_silu", "dt_and_decay",
     "ssm_scan_sequential", "ssd_chunked", "gated_group_rmsnorm",
     "mixer_sequence", "mixer_decode", "mixer_prefill",
+    "mixer_decode_bf16_state", "mixer_prefill_bf16_state",
 ]
 
 # NemotronH Mamba2 mixer geometry: hidden 2688, in_proj 2688 -> 10304 and
@@ -485,4 +486,42 @@ def mixer_prefill(p, hidden_bf16, cu_seqlens, slot_idx, has_initial, ssm_pool, c
         conv_pool[s] = r["window"]
         out[t0:t1] = r["out"]
         res.append(r)
+    return out, res
+
+
+# ----------------------------------------------------------------------------
+# bf16 SSM state pool
+# ----------------------------------------------------------------------------
+
+def _widen_state(ssm_pool_bf16):
+    """The f32 working copy of a bf16 state pool (exact: every bf16 value is a float32)."""
+    return bf16_to_f64(ssm_pool_bf16).astype(np.float32)
+
+
+def mixer_decode_bf16_state(p, hidden_bf16, slot_idx, ssm_pool_bf16, conv_pool, g=GEOMETRY):
+    """mixer_decode with the SSM state stored as bfloat16 [S, H, P, N] (bit patterns).
+
+    [PR1288] "What it does": the gather widens the stored rows into an f32 working buffer
+    and the result is narrowed back to the cache dtype, so a bf16 cache is a different
+    computation from an f32 one. Read that way: widen the rows (exact), run the f32
+    computation of mixer_decode unchanged (outputs come from the f32 state), then round
+    each touched row's f32 state to bf16 (round half to even). Updates ssm_pool_bf16 and
+    conv_pool in place; returns what mixer_decode returns.
+    """
+    work = _widen_state(ssm_pool_bf16)
+    out, res = mixer_decode(p, hidden_bf16, slot_idx, work, conv_pool, g)
+    for s in sorted({int(s) for s in slot_idx if int(s) >= 0}):
+        ssm_pool_bf16[s] = bf16_from_f64(work[s])
+    return out, res
+
+
+def mixer_prefill_bf16_state(p, hidden_bf16, cu_seqlens, slot_idx, has_initial, ssm_pool_bf16, conv_pool,
+                             g=GEOMETRY):
+    """mixer_prefill with a bfloat16 state pool, read as mixer_decode_bf16_state: the
+    initial rows are widened to f32, the call runs as mixer_prefill, and every sequence's
+    final f32 state is rounded to bf16 into its row."""
+    work = _widen_state(ssm_pool_bf16)
+    out, res = mixer_prefill(p, hidden_bf16, cu_seqlens, slot_idx, has_initial, work, conv_pool, g)
+    for s in sorted({int(s) for s in slot_idx}):
+        ssm_pool_bf16[s] = bf16_from_f64(work[s])
     return out, res

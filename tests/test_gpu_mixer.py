@@ -15,6 +15,10 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 TOL_OUT, TOL_STATE = 2e-2, 1e-3
+# bf16 state pool: two f32 states within eps of each other round to bf16 values one ulp
+# (2^-8 relative) apart on about eps / ulp of the elements, an RMS of sqrt(eps * 2^-8) =
+# 2e-3 at the stated f32 bar eps = 1e-3; twice that is the bar
+TOL_STATE_BF16 = 4e-3
 H, I = 2688, 4096
 
 
@@ -277,6 +281,75 @@ def test_mixed_batch_decode_rows_and_prefill_chunks(nhm, block0):
         a, b = bf16_to_f64(cpd[s]), bf16_to_f64(cpg[s])
         assert rel_l2(a, b) <= TOL_STATE and rel_max(a, b) <= TOL_OUT
     print(f"mixed batch {lens}: {m}, state rel l2 {st:.3e}")
+
+
+def _check_states_bf16(sp_gpu, sp_ref, sp_before, touched):
+    from oracle import bf16_to_f64
+    from tests.gpu_util import rel_l2
+    worst = 0.0
+    for s in range(sp_ref.shape[0]):
+        if s in touched and not np.any(sp_ref[s]):
+            assert not np.any(sp_gpu[s]), f"slot {s} should be zero"
+        elif s in touched:
+            r = rel_l2(bf16_to_f64(sp_gpu[s]), bf16_to_f64(sp_ref[s]))
+            worst = max(worst, r)
+            assert r <= TOL_STATE_BF16, f"slot {s}: bf16 state rel l2 {r:.3g}"
+        else:
+            assert np.array_equal(sp_gpu[s], sp_before[s]), f"untouched slot {s} changed"
+    return worst
+
+
+def test_decode_bf16_state_two_steps(nhm, block0):
+    """Decode B=8 (one padded row) for two steps on a bf16 state pool: the second step reads
+    the state the first rounded. Outputs and every pool row against the oracle's bf16-state
+    decode."""
+    from oracle import mixer_decode_bf16_state
+    from tests.gpu_util import upload_params
+    from workloads import bf16_bits, conv_pool, hidden, slots, ssm_pool
+    S, B = 16, 8
+    sl = slots(2, B, S)
+    sl[3] = -1
+    sp = bf16_bits(ssm_pool(2, 3, S))
+    cp = conv_pool(2, 3, S)
+    pd = upload_params(block0)
+    spr, cpr = sp.copy(), cp.copy()
+    live = [b for b in range(B) if sl[b] >= 0]
+    touched = {int(s) for s in sl if s >= 0}
+    for step in range(2):
+        h = hidden(2, B, extra=40 + step)
+        out, spg, cpg, ws, lay = _gpu_decode(nhm, pd, h, sl, sp, cp)
+        before = sp.copy()
+        ref, res = mixer_decode_bf16_state(block0, h, sl, spr, cpr)
+        m = _parity(out, ws, lay, live, ref, res["norm"][live], res["q_out"][live], block0)
+        assert np.all(out[3] == 0)
+        st = _check_states_bf16(spg, spr, before, touched)
+        _check_windows(cpg, cpr, cp, touched)
+        sp, cp = spg, cpg                       # the GPU's rounded state feeds the next step
+        spr, cpr = spg.copy(), cpg.copy()       # and the oracle starts from the same rows
+        print(f"decode bf16 state, step {step}: {m}, state rel l2 {st:.3e}")
+
+
+@pytest.mark.parametrize("lens,has_init", [([5, 130, 1, 0, 260, 128], [1, 0, 1, 0, 1, 0])])
+def test_prefill_bf16_state(nhm, block0, lens, has_init):
+    from oracle import mixer_prefill_bf16_state
+    from tests.gpu_util import upload_params
+    from workloads import bf16_bits, conv_pool, hidden, ssm_pool
+    S = 8
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    h = hidden(4, T, extra=50)
+    sp, cp = bf16_bits(ssm_pool(4, 3, S)), conv_pool(4, 3, S)
+    sl = np.array([7, 0, 3, 5, 1, 6][:len(lens)], np.int32)
+    pd = upload_params(block0)
+    out, spg, cpg, ws, lay = _gpu_prefill(nhm, pd, h, cu, sl, has_init, sp, cp)
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_prefill_bf16_state(block0, h, cu, sl, has_init, spr, cpr)
+    norm, q, _ = _prefill_refs(res, lens)
+    m = _parity(out, ws, lay, list(range(T)), ref, norm, q, block0)
+    touched = set(int(s) for s in sl)
+    st = _check_states_bf16(spg, spr, sp, touched)
+    _check_windows(cpg, cpr, cp, touched)
+    print(f"prefill bf16 state {lens}: {m}, state rel l2 {st:.3e}")
 
 
 def test_decode_equals_prefill_of_one(nhm, block0):
