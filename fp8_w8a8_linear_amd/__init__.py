@@ -13,7 +13,7 @@ import os
 __all__ = ["lib", "LIB_PATH", "NhmError", "Geometry", "Layout", "WsLayout", "Fp8Weight", "MixerParams",
            "GEOMETRY", "mixer_layout", "quantize_static", "fp8_linear", "fp8_linear_workspace_bytes",
            "decode_ws_layout", "prefill_ws_layout", "mixer_decode", "mixer_prefill", "NHM_BF16", "NHM_E4M3",
-           "NHM_F32"]
+           "NHM_F32", "fp8_dequant_channel_bf16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnhm.so")
 if not os.path.exists(LIB_PATH):
@@ -66,6 +66,7 @@ _SIGS = {
     "nhm_mixer_layout": (C.c_int, [C.POINTER(Geometry), C.POINTER(Layout)]),
     "nhm_fp8_quantize_static": (C.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "nhm_fp8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int]),
+    "nhm_fp8_dequant_channel_bf16": (C.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     "nhm_fp8_linear": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, _i64, _p, _sz, _p]),
     "nhm_fp8_linear_ex": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, C.c_int, _i64, _p, _sz, _p]),
     "nhm_mixer_decode_ws_layout": (C.c_int, [C.POINTER(Geometry), _i32, C.POINTER(WsLayout)]),
@@ -188,6 +189,18 @@ def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None
         ws = torch.zeros(need, dtype=torch.uint8, device=a.device)
     _check(lib.nhm_fp8_linear_ex(_ptr(a), a_type, m, a.shape[1], C.byref(weight.struct), _ptr(out), out_type,
                                  out.shape[1], _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def fp8_dequant_channel_bf16(w, w_scale, out=None, stream=None):
+    """bf16 [n, k] = bf16(val(w) * w_scale[row]) of an e4m3 weight [n, k] (uint8)."""
+    import torch
+    w = _dev_tensor(w, "w")
+    n, k = int(w.shape[0]), int(w.shape[1])
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int16, device=w.device)
+    _check(lib.nhm_fp8_dequant_channel_bf16(_ptr(w), _ptr(w_scale), n, k, w.stride(0), _ptr(out), out.stride(0),
+                                            _stream(stream)))
     return out
 
 

@@ -203,6 +203,21 @@ nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t cols
     return check_launch("quantize_static");
 }
 
+nhm_status nhm_fp8_dequant_channel_bf16(const uint8_t* w, const float* w_scale, int64_t n, int64_t k, int64_t ld_w,
+                                        uint16_t* out, int64_t ld_out, void* stream) {
+    g_err[0] = 0;
+    if (n < 0 || k < 0) return fail(NHM_ERR_SHAPE, "negative n/k (%lld, %lld)", (long long)n, (long long)k);
+    if (n == 0 || k == 0) return NHM_OK;
+    if (!w || !w_scale || !out) return fail(NHM_ERR_NULL, "w, w_scale or out is NULL");
+    if (k % 16 != 0 || ld_w < k || ld_out < k)
+        return fail(NHM_ERR_SHAPE, "k %lld must be a multiple of 16 and ld_w %lld, ld_out %lld >= k", (long long)k,
+                    (long long)ld_w, (long long)ld_out);
+    if (!aligned(w, 16) || !aligned(out, 16) || !aligned(w_scale, 4) || ld_w % 16 != 0 || ld_out % 8 != 0)
+        return fail(NHM_ERR_ALIGN, "w and out must be 16-byte aligned with 16-byte row strides");
+    launch_dequant_channel(w, n, k, ld_w, w_scale, out, ld_out, (hipStream_t)stream);
+    return check_launch("dequant_channel_bf16");
+}
+
 size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type) {
     if (m <= 0 || n <= 0 || k <= 0) return 0;
     return linear_ws(m, k, a_type);

@@ -21,6 +21,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                      uint8_t* q, int64_t ld_q, hipStream_t st);
 
+// per-channel e4m3 -> bf16 weight dequant (quant.hip); cols a multiple of 16, 16-byte rows
+void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_t ld_w, const float* w_scale,
+                            uint16_t* out, int64_t ld_out, hipStream_t st);
+
 // ---- weight-streaming GEMV for m <= 16 (gemv.hip)
 
 // Epilogue of the in_proj GEMV inside a decode step: besides storing the bf16

@@ -55,3 +55,47 @@ void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x
 }
 
 }  // namespace nhm
+
+namespace nhm {
+
+// Per-output-channel FP8 -> bf16 weight dequant (the standalone device dequant of the
+// W8A16 arm): out[r, c] = bf16(val(w[r, c]) * w_scale[r]), the product in f32 and rounded
+// once to bf16 (half to even). HBM-bound: 1 byte in, 2 bytes out per element; each thread
+// takes 16 codes (one 16-byte load, two 16-byte stores). The codes convert to bf16
+// exactly (every e4m3 value is a bf16 value; NaN codes stay NaN).
+__global__ __launch_bounds__(256) void dequant_channel_kernel(const uint8_t* __restrict__ w, int64_t rows,
+                                                             int64_t vec_per_row, int64_t ld_w,
+                                                             const float* __restrict__ w_scale,
+                                                             uint16_t* __restrict__ out, int64_t ld_out) {
+    const int64_t total = rows * vec_per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / vec_per_row, v = i - r * vec_per_row;
+        const uint4 codes = *reinterpret_cast<const uint4*>(w + r * ld_w + v * 16);
+        const float s = w_scale[r];
+        const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bf16x8 b = e4m3x8_to_bf16(cw[2 * h], cw[2 * h + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[4 * h + j] = f32x2_to_bf16x2((float)b[2 * j] * s, (float)b[2 * j + 1] * s);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(out + r * ld_out + v * 16);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_t ld_w, const float* w_scale,
+                            uint16_t* out, int64_t ld_out, hipStream_t st) {
+    if (rows <= 0 || cols <= 0) return;
+    const int64_t work = rows * (cols / 16);
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    dequant_channel_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, rows, cols / 16, ld_w, w_scale, out,
+                                                                        ld_out);
+}
+
+}  // namespace nhm

@@ -146,6 +146,22 @@ typedef struct nhm_fp8_weight {
 NHM_API nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                    const float* scale, uint8_t* q, int64_t ld_q, void* stream);
 
+/* Per-output-channel dequant of an e4m3 weight to bf16 ([PR950] "What runs where, and
+ * why the line falls there": the one standalone device dequant is per-channel FP8 ->
+ * bf16), the building block of the W8A16 reference the pages compare the W8A8 arm
+ * against ([PR1288] "The comparison is not bit-comparable, and that is the point": the
+ * host arm is W8A16, its input_scale carried and not applied). A debug and
+ * counterfactual op, not on the W8A8 path:
+ *   out[r, c] = bf16( val(w[r, c]) * w_scale[r] ), the product in f32, rounded once
+ *   (half to even); NaN codes give NaN.
+ *   w       (device) e4m3 [n, ld_w], 16-byte aligned, ld_w % 16 == 0
+ *   w_scale (device) f32 [n]
+ *   out     (device) bf16 [n, ld_out], 16-byte aligned, ld_out % 8 == 0; must not overlap w
+ * k must be a multiple of 16 and ld_w, ld_out >= k. n == 0 or k == 0 is a valid no-op.
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_HIP. */
+NHM_API nhm_status nhm_fp8_dequant_channel_bf16(const uint8_t* w, const float* w_scale, int64_t n, int64_t k,
+                                        int64_t ld_w, uint16_t* out, int64_t ld_out, void* stream);
+
 /* Workspace bytes nhm_fp8_linear needs for this shape and input type. */
 NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type);
 

@@ -52,7 +52,7 @@ __all__ = [
     "quantize_static", "fp8_linear", "causal_conv1d_silu", "dt_and_decay",
     "ssm_scan_sequential", "ssd_chunked", "gated_group_rmsnorm",
     "mixer_sequence", "mixer_decode", "mixer_prefill",
-    "mixer_decode_bf16_state", "mixer_prefill_bf16_state",
+    "mixer_decode_bf16_state", "mixer_prefill_bf16_state", "dequant_channel_bf16",
 ]
 
 # NemotronH Mamba2 mixer geometry: hidden 2688, in_proj 2688 -> 10304 and
@@ -525,3 +525,22 @@ def mixer_prefill_bf16_state(p, hidden_bf16, cu_seqlens, slot_idx, has_initial, 
     for s in sorted({int(s) for s in slot_idx}):
         ssm_pool_bf16[s] = bf16_from_f64(work[s])
     return out, res
+
+
+# ----------------------------------------------------------------------------
+# W8A16 weight dequant (debug / counterfactual arm)
+# ----------------------------------------------------------------------------
+
+def dequant_channel_bf16(w_codes, w_scale):
+    """Per-output-channel e4m3 -> bf16 dequant: bf16(val(W[r, c]) * ws[r]) as bit patterns.
+
+    [PR950] "What runs where, and why the line falls there" names the one standalone
+    device dequant, per-channel FP8 -> bf16; [PR1288] "The comparison is not
+    bit-comparable, and that is the point": the host arm it serves is W8A16, the weight
+    dequantized to bf16 and the activation left unquantized. Read as the path's stage
+    rule (f32 inside a stage, bf16 at its boundary): the product is formed in float32
+    (IEEE, round to nearest) and rounded once to bf16 (half to even). NaN codes give NaN.
+    """
+    v = e4m3_decode(w_codes).astype(np.float32)          # exact: every e4m3 value is a float32
+    prod = v * np.asarray(w_scale, np.float32).reshape(-1, 1)
+    return bf16_from_f64(prod.astype(np.float64))

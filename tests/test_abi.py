@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(nhm):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(nhm.lib, n), f"{n} not exported"
 
@@ -96,6 +96,21 @@ def test_linear_ex_refusals(nhm):
 
 def test_linear_zero_rows_is_noop(nhm):
     assert _lin(nhm, None, nhm.NHM_BF16, 0, 128, _w(nhm), None, 64, None, 0) == 0
+
+
+def test_dequant_refusals(nhm):
+    d = nhm.lib.nhm_fp8_dequant_channel_bf16
+    W, S, O = 0x10000, 0x20000, 0x30000
+    assert d(None, None, 0, 16, 16, None, 16, None) == 0                 # empty is a no-op
+    assert d(W, S, 4, 0, 16, O, 16, None) == 0
+    assert d(None, S, 4, 16, 16, O, 16, None) == 1
+    assert d(W, S, 4, 16, 16, None, 16, None) == 1
+    assert d(W, S, -1, 16, 16, O, 16, None) == 2
+    assert d(W, S, 4, 24, 32, O, 32, None) == 2                           # k % 16 != 0
+    assert d(W, S, 4, 16, 8, O, 16, None) == 2                            # ld_w < k
+    assert d(W + 8, S, 4, 16, 16, O, 16, None) == 3
+    assert d(W, S, 4, 16, 24, O, 16, None) == 3                           # ld_w % 16 != 0
+    assert d(W, S, 4, 16, 16, O + 4, 16, None) == 3
 
 
 def test_quant_refusals(nhm):
