@@ -74,7 +74,8 @@ def test_linear_sweep_shapes(nhm, m, n, k):
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
                                    (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
                                    (384, 10300, 2608), (500, 10000, 2672), (641, 130, 256), (700, 520, 272),
-                                   (2600, 4100, 272), (1030, 10304, 2688)])
+                                   (2600, 4100, 272), (1030, 10304, 2688),
+                                   (3, 520, 12288), (2, 130, 16384)])     # the GEMV's 16-wave variants
 def test_linear_ragged(nhm, m, n, k):
     from workloads import linear_case
     a, w, ws, sa = linear_case(m, n, k, extra=7)

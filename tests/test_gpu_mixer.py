@@ -124,12 +124,12 @@ def test_decode_one_block_one_token(nhm, block0):
     print(f"decode m=1: {m}, state rel l2 {st:.3e}")
 
 
-@pytest.mark.parametrize("B,slot_list", [(8, None), (3, [5, -1, 0]), (20, None)])
-def test_decode_batch(nhm, block0, B, slot_list):
+@pytest.mark.parametrize("B,slot_list,S", [(8, None, 24), (3, [5, -1, 0], 24), (20, None, 24),
+                                           (64, None, 64)])        # the whole 64-slot pool in one call
+def test_decode_batch(nhm, block0, B, slot_list, S):
     from oracle import mixer_decode
     from tests.gpu_util import upload_params
     from workloads import conv_pool, hidden, slots, ssm_pool
-    S = 24
     h = hidden(2, B, extra=B)
     sl = np.array(slot_list, np.int32) if slot_list else slots(2, B, S)
     sp, cp = ssm_pool(2, 0, S), conv_pool(2, 0, S)
