@@ -26,11 +26,23 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
     const int slot = a.slot_idx[b];
     __shared__ float sx[kP], sB[kN], sC[kN];
 
+    // The small operands first, together with the slot index, branch-free (clamped indexes;
+    // row b of the workspace exists for a padded row too), then the state stream: loads
+    // complete in issue order, so staging x, B and C waits for these alone, not for the state.
+    // Thread t < 64 takes x[t]; t < 128 takes B[t], the others C[t - 128].
+    const uint16_t* xr = a.xbc_conv + (int64_t)b * a.conv_dim;
+    const uint32_t xu = xr[h * kP + (t & (kP - 1))];
+    const uint32_t bcu = xr[(t < kN ? a.b_off + g * kN + t : a.c_off + g * kN + t - kN)];
+    const uint32_t dtu = a.zxbcdt[(int64_t)b * a.d_in_proj + a.dt_off + h];
+    const float A_log = a.A_log[h], dt_bias = a.dt_bias[h], Dh = a.D[h];
+    asm volatile("" ::: "memory");   // keep the loads above ahead of the state stream
+
     uint16_t* yrow = a.y + (int64_t)b * a.d_inner + h * kP;
     if (slot < 0) {                      // padded row: zero output, no state touched
         if (t < kP) yrow[t] = 0;
         return;
     }
+
     // element e = 4 * (t + 256 i): p = t / 32 + 8 i, n = 4 * (t % 32) .. + 3
     const int64_t row0 = (((int64_t)slot * a.n_heads + h) * kP) * kN;
     v4f* st = reinterpret_cast<v4f*>(a.ssm_pool + (kBf16 ? 0 : row0));
@@ -46,12 +58,11 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
         }
     }
 
-    const uint16_t* xr = a.xbc_conv + (int64_t)b * a.conv_dim;
-    if (t < kP) sx[t] = bf16_to_f32(xr[h * kP + t]);
-    if (t < kN) sB[t] = bf16_to_f32(xr[a.b_off + g * kN + t]);
-    else sC[t - kN] = bf16_to_f32(xr[a.c_off + g * kN + t - kN]);
-    const float dt = softplus(bf16_to_f32(a.zxbcdt[(int64_t)b * a.d_in_proj + a.dt_off + h]) + a.dt_bias[h]);
-    const float dA = __expf(dt * -__expf(a.A_log[h]));
+    if (t < kP) sx[t] = bf16_to_f32(xu);
+    if (t < kN) sB[t] = bf16_to_f32(bcu);
+    else sC[t - kN] = bf16_to_f32(bcu);
+    const float dt = softplus(bf16_to_f32(dtu) + dt_bias);
+    const float dA = __expf(dt * -__expf(A_log));
     __syncthreads();
 
     const int n0 = 4 * (t & 31);
@@ -80,7 +91,6 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
         for (int o = 16; o >= 1; o >>= 1) yp[i] += __shfl_xor(yp[i], o, kWave);
     }
     if ((t & 31) == 0) {
-        const float Dh = a.D[h];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int p = (t >> 5) + 8 * i;

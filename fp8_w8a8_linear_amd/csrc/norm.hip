@@ -24,11 +24,12 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     const uint16_t* yr = a.y + tok * a.d_inner + (int64_t)g * gw;
     const uint16_t* zr = a.zxbcdt + tok * a.d_in_proj + a.z_off + (int64_t)g * gw;
     const float so = *a.out_a_scale;
-    const bool fast = fast_scale(so);    // the quant's reciprocal form (exact; see quant_bf16x8_fast)
-    const float rso = __fdiv_rn(1.0f, so);
-    auto emit = [&](int c, const float (&v)[8], float r) {
+    // emit(c, v, r, nw): nw holds norm_w[c .. c + 7] (loaded with y and z where possible)
+    auto emit = [&](int c, const float (&v)[8], float r, const uint4 nw) {
+        const bool fast = fast_scale(so);    // the quant's reciprocal form (exact; see quant_bf16x8_fast)
+        const float rso = __fdiv_rn(1.0f, so);
         float w[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c), w);
+        unpack8(nw, w);
         uint32_t ob[4];   // bf16 pairs
 #pragma unroll
         for (int j = 0; j < 4; ++j) ob[j] = f32x2_to_bf16x2(v[2 * j] * r * w[2 * j], v[2 * j + 1] * r * w[2 * j + 1]);
@@ -43,14 +44,17 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     float ss = 0.f;
     if constexpr (kIt > 0) {
         float v[kIt][8];
-        uint4 yv[kIt], zv[kIt];
+        uint4 yv[kIt], zv[kIt], wv[kIt];
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {                 // all loads first
+        for (int it = 0; it < kIt; ++it) {                 // all loads first (norm weights too)
             const int c = lane * 8 + it * 512;
             const int cc = c < gw ? c : 0;                 // in bounds; masked below
             yv[it] = *reinterpret_cast<const uint4*>(yr + cc);
             zv[it] = *reinterpret_cast<const uint4*>(zr + cc);
+            wv[it] = *reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + cc);
         }
+        // the scale's scalar load goes out with them, not after the reduction
+        asm volatile("" ::"s"(so) : "memory");
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
             float y[8], z[8];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
             const int c = lane * 8 + it * 512;
-            if (c < gw) emit(c, v[it], r);
+            if (c < gw) emit(c, v[it], r, wv[it]);
         }
     } else {
         for (int c = lane * 8; c < gw; c += 64 * 8) {
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
             unpack8(*reinterpret_cast<const uint4*>(zr + c), z);
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = y[j] * silu(z[j]);
-            emit(c, v, r);
+            emit(c, v, r, *reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c));
         }
     }
 }

@@ -6,24 +6,44 @@
 
 namespace nhm {
 
-// Eight elements per thread: one 16-byte load, one 8-byte store.
+// Eight elements per thread: one 16-byte load, one 8-byte store. The first element's load
+// goes out before the scale is read (at decode sizes each thread has one element, and the two
+// round trips overlap); row indexes use 32-bit division when the element count allows.
 __global__ __launch_bounds__(256) void quant_vec8_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                         int64_t vec_per_row, int64_t ld_x,
                                                         const float* __restrict__ scale,
                                                         uint8_t* __restrict__ q, int64_t ld_q) {
-    const float s = *scale;
     const int64_t total = rows * vec_per_row;
+    const bool narrow = total < (int64_t(1) << 31);
+    auto split = [&](int64_t i, int64_t& r, int64_t& v) {
+        if (narrow) {
+            const uint32_t rr = (uint32_t)i / (uint32_t)vec_per_row;
+            r = rr;
+            v = (uint32_t)i - rr * (uint32_t)vec_per_row;
+        } else {
+            r = i / vec_per_row;
+            v = i - r * vec_per_row;
+        }
+    };
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    int64_t r, v;
+    split(i, r, v);
+    uint4 in = *reinterpret_cast<const uint4*>(x + r * ld_x + v * 8);
+    asm volatile("" ::: "memory");   // the first load ahead of the scale
+    const float s = *scale;
     // the scale is uniform: one branch picks the reciprocal form or the IEEE division
     const bool fast = fast_scale(s);
     const float rs = __fdiv_rn(1.0f, s);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / vec_per_row, v = i - r * vec_per_row;
-        const uint4 in = *reinterpret_cast<const uint4*>(x + r * ld_x + v * 8);
+    for (;;) {
         uint2 code;
         if (fast && __builtin_amdgcn_ballot_w64(bf16x8_special(in) != 0u) == 0) code = quant_bf16x8_fast(in, s, rs);
         else code = quant_bf16x8(in, s);
         *reinterpret_cast<uint2*>(q + r * ld_q + v * 8) = code;
+        i += (int64_t)gridDim.x * blockDim.x;
+        if (i >= total) break;
+        split(i, r, v);
+        in = *reinterpret_cast<const uint4*>(x + r * ld_x + v * 8);
     }
 }
 
