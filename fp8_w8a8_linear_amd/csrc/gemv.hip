@@ -25,6 +25,7 @@ struct GemvArgs {
     uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
     float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
     int ksteps;
+    int rows;                                       // features per workgroup: 16, or a multiple of 4 below
     ConvEpilogue conv;
 };
 
@@ -34,8 +35,9 @@ template <int kWaves, int kSteps, bool kConv>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t row = n0 + (lane & 15);       // A operand row (feature)
+    const int64_t n0 = (int64_t)blockIdx.x * g.rows;
+    const int64_t row = n0 + (lane & 15);       // A operand row (feature); rows past g.rows load zeros
+    const int64_t nend = n0 + g.rows < g.n ? n0 + g.rows : g.n;   // this workgroup's features end
     const int col = lane & 15;                  // B operand column (token)
     const int kq = (lane >> 4) * 32;
     const int64_t nbase = n0 + 4 * (lane >> 4);
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
-    const uint32_t wrow = row < g.n ? (uint32_t)(row * g.k) : kGemvOut;
+    const uint32_t wrow = row < nend ? (uint32_t)(row * g.k) : kGemvOut;
     const uint32_t arow = col < g.m ? (uint32_t)(col * g.lda) : kGemvOut;
     // weight and activation pieces of each k-step are issued together
     v8i wa[kSteps], xb[kSteps];
@@ -113,11 +115,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     if (col >= g.m) return;
     if (g.out_f32) {   // (never with the conv epilogue)
         float* of = g.out_f32 + (int64_t)col * g.ld_out + nbase;
-        if (g.vec_out && nbase + 3 < g.n) {
+        if (g.vec_out && nbase + 3 < nend) {
             *reinterpret_cast<float4*>(of) = make_float4(acc[0] * sc[0], acc[1] * sc[1], acc[2] * sc[2], acc[3] * sc[3]);
         } else {
             for (int r = 0; r < 4; ++r)
-                if (nbase + r < g.n) of[r] = acc[r] * sc[r];
+                if (nbase + r < nend) of[r] = acc[r] * sc[r];
         }
         return;
     }
@@ -125,11 +127,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[r] * sc[r]);
     uint16_t* o = g.out + (int64_t)col * g.ld_out + nbase;
-    if (g.vec_out && nbase + 3 < g.n) {
+    if (g.vec_out && nbase + 3 < nend) {
         *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
     } else {
         for (int r = 0; r < 4; ++r)
-            if (nbase + r < g.n) o[r] = (uint16_t)hb[r];
+            if (nbase + r < nend) o[r] = (uint16_t)hb[r];
     }
 
     if constexpr (kConv) {
@@ -186,7 +188,17 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     const int waves = g.ksteps < 24 ? 4 : (g.ksteps <= 8 * kGemvMaxSteps ? 8 : 16);
     const int per = (g.ksteps + waves - 1) / waves;
     const int steps = per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
-    const dim3 grid((unsigned)((n + 15) / 16));
+    // 16 features per workgroup; where that leaves CUs idle (n < 16 x 256), fewer features
+    // per workgroup, a multiple of 4 (whole 4-feature stores), so that the workgroups cover
+    // more CUs: each CU streams its share of the weight at a rate bounded by the requests it
+    // can keep in flight, so the weight is delivered faster over more CUs (the spare MFMA rows
+    // load zeros). The conv epilogue keeps 16.
+    g.rows = 16;
+    if (!conv && n < 16 * 256) {
+        const int64_t per = (n + 255) / 256;
+        g.rows = per <= 4 ? 4 : (int)((per + 3) / 4 * 4);
+    }
+    const dim3 grid((unsigned)((n + g.rows - 1) / g.rows));
 #define NHM_GEMV_LAUNCH(W, S)                                                  \
     do {                                                                       \
         if (conv) gemv_kernel<W, S, true><<<grid, dim3(W * 64), 0, st>>>(g);  \
