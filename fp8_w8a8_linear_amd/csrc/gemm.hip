@@ -25,6 +25,8 @@
 //    per MAC of a 128 x 128 tile, which is what bounds this GEMM on the L2 -> CU path.
 //  * 128 x 128 tile kernel (remaining shapes): both operands staged through
 //    double-buffered LDS, four waves of 64 x 64.
+#include <stdint.h>
+
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -340,15 +342,19 @@ constexpr int kWT = 256;               // workgroup tile extent in n (and in m f
 constexpr int kWK = 64;                // k bytes per ring stage (one 32x32x64 MFMA deep)
 constexpr int kWStage = kWT * kWK;     // the weight tile's part of a stage, 16 KB
 
-// Ring geometry of a 256 (n) x TM (m) tile: a stage holds 256 weight rows then TM activation
-// rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for TM = 256, 6 x 24 KB
-// for TM = 128).
-template <int TM>
+// Ring geometry of a TN (n) x TM (m) tile: a stage holds TN weight rows then TM activation
+// rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for 256 x 256, 6 x 24 KB
+// for 256 x 128, 8 x 20 KB for 192 x 128). The eight waves are 2 (n) x 4 (m), each TN / 2 x
+// TM / 4. A stage is (TN + TM) / 16 DMA blocks of 16 rows (1 KB each, block b at b KB of the
+// stage); each wave issues kLoads of them per stage.
+template <int TN, int TM>
 struct RingShape {
-    static constexpr int kStage = (kWT + TM) * kWK;
+    static constexpr int kStage = (TN + TM) * kWK;
     static constexpr int kRing = (160 * 1024) / kStage;
+    static constexpr int kNI = TN / 64;           // 32-row weight blocks per wave (wave tile n = TN / 2)
     static constexpr int kJX = TM / 128;          // 32-row activation blocks per wave (wave tile m = TM / 4)
-    static constexpr int kLoads = 2 + kJX;        // 16-row DMA instructions per wave per stage
+    static constexpr int kBlocks = (TN + TM) / 16;
+    static constexpr int kLoads = (kBlocks + 7) / 8;   // DMA instructions per wave per stage
 };
 
 __device__ __forceinline__ v16f mfma32_e4m3(const v8i& a, const v8i& b, const v16f& c) {
@@ -394,66 +400,80 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Operands under 2^31 bytes (buffer offsets). Grid = number of 256 x TM tiles, 512 threads.
-template <int TM>
+// Operands under 2^31 bytes (buffer offsets). Grid = number of TN x TM tiles, 512 threads.
+template <int TN, int TM>
 __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
-    using RS = RingShape<TM>;
-    constexpr int kStage = RS::kStage, kRing = RS::kRing, kJX = RS::kJX, kLoads = RS::kLoads;
-    static_assert(TM == 256 || TM == 128, "tile m extent");
+    using RS = RingShape<TN, TM>;
+    constexpr int kStage = RS::kStage, kRing = RS::kRing, kNI = RS::kNI, kJX = RS::kJX, kLoads = RS::kLoads;
+    constexpr int kWStageT = TN * kWK;              // the weight rows' part of a stage
+    static_assert((TN == 256 && (TM == 256 || TM == 128)) || (TN == 192 && TM == 128), "tile shape");
     static_assert(kRing >= 4 && (kRing - 2) * kLoads < 64, "ring depth and the vmcnt field");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
-    static_assert(kRing * kStage >= TM * kWT * 2, "the epilogue stages the whole bf16 tile in the ring");
+    // the epilogue stages the bf16 tile in the ring as TM rows of 512 bytes (TN <= 256)
+    static_assert(kRing * kStage >= TM * 512, "the epilogue stages the whole bf16 tile in the ring");
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n 128 x m TM / 4
+    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n TN / 2 x m TM / 4
     const int r32 = lane & 31, q = lane >> 5;
 
     // Blocks go to the 8 XCDs round robin; each XCD takes a contiguous share of the tiles in an
     // order that walks 8 m-tiles per n-tile, so the ~32 tiles an XCD holds at once share 8
     // activation and 4 weight panels through its L2.
-    const int ntn = (int)((g.n + kWT - 1) / kWT), ntm = (int)((g.m + TM - 1) / TM);
+    const int ntn = (int)((g.n + TN - 1) / TN), ntm = (int)((g.m + TM - 1) / TM);
     const int total = ntn * ntm;
     const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
     const int j = x * (total >> 3) + min(x, total & 7) + loc;
     constexpr int kGroupM = 8;
     const int grp = j / (kGroupM * ntn), within = j - grp * kGroupM * ntn;
     const int gms = min(kGroupM, ntm - grp * kGroupM);
-    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * TM, n0 = (int64_t)(within / gms) * kWT;
+    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * TM, n0 = (int64_t)(within / gms) * TN;
 
-    // DMA: wave w fills weight rows 32 w .. 32 w + 31 and activation rows (TM / 8) w ..
-    // (TM / 8) (w + 1) - 1 of a stage, 16 rows per instruction; lane l lands in slot l of the
-    // instruction's 1 KB: row 16 i + l / 4, chunk slot l % 4, which holds the logical chunk
-    // kc / 16 under the swizzle (the swizzle depends on the row modulo 16 only).
+    // DMA. TN = 256: wave w fills weight rows 32 w .. 32 w + 31 and activation rows (TM / 8) w
+    // .. (TM / 8) (w + 1) - 1 of a stage. TN = 192: wave w takes the 16-row blocks w, w + 8,
+    // w + 16 of the stage's 20 (weight blocks first); where w + 16 is past the last block it
+    // loads block w + 8 a second time (the same bytes to the same place), so that every wave
+    // issues kLoads instructions per stage and the waits count alike. 16 rows per instruction;
+    // lane l lands in slot l of the instruction's 1 KB: row 16 i + l / 4, chunk slot l % 4,
+    // which holds the logical chunk kc / 16 under the swizzle (the swizzle depends on the row
+    // modulo 16 only).
     const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
     const int lr = lane >> 2;
     const int kc = ((lane & 3) ^ (((lr >> 1) ^ (lr >> 2)) & 3)) * 16;
-    uint32_t wb[2], ab[kJX];
+    uint32_t dbase[kLoads];    // this lane's source offset of each of the wave's blocks (k = 0)
+    int dlds[kLoads];          // the block's byte offset in a stage
+    bool dw[kLoads];           // weight block (else activation)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = wave * 32 + i * 16 + lr;
-        wb[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
-    }
-#pragma unroll
-    for (int i = 0; i < kJX; ++i) {
-        const int row = wave * (TM / 8) + i * 16 + lr;
-        ab[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
+    for (int i = 0; i < kLoads; ++i) {
+        int blk;
+        if constexpr (TN == 256) {
+            blk = i < 2 ? wave * 2 + i : RS::kBlocks - TM / 16 + wave * kJX + (i - 2);
+        } else {
+            blk = wave + 8 * i;
+            if (blk >= RS::kBlocks) blk -= 8;
+        }
+        dw[i] = blk < TN / 16;
+        dlds[i] = blk * 1024;
+        if (dw[i]) {
+            const int row = blk * 16 + lr;
+            dbase[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
+        } else {
+            const int row = (blk - TN / 16) * 16 + lr;
+            dbase[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
+        }
     }
     auto issue = [&](int s) {   // stage s (s may run past k: its loads are out of range, zeros)
         const uint32_t k0 = (uint32_t)s * kWK;
         const bool kin = (int64_t)k0 + kc < g.k;
         uint8_t* sb = smem + (s % kRing) * kStage;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(wrs, sb + (wave * 32 + i * 16) * kWK, kin ? wb[i] + k0 : kOutOfRange);
-#pragma unroll
-        for (int i = 0; i < kJX; ++i)
-            dma16(ars, sb + kWStage + (wave * (TM / 8) + i * 16) * kWK, kin ? ab[i] + k0 : kOutOfRange);
+        for (int i = 0; i < kLoads; ++i) dma16(dw[i] ? wrs : ars, sb + dlds[i], kin ? dbase[i] + k0 : kOutOfRange);
     };
-    auto read_ops = [&](int s, v8i (&wop)[4], v8i (&aop)[kJX]) {
+    auto read_ops = [&](int s, v8i (&wop)[kNI], v8i (&aop)[kJX]) {
         const uint8_t* sw = smem + (s % kRing) * kStage;
-        const uint8_t* sa = sw + kWStage;
+        const uint8_t* sa = sw + kWStageT;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wn * 128 + i * 32 + r32;
+        for (int i = 0; i < kNI; ++i) {
+            const int row = wn * (TN / 2) + i * 32 + r32;
             wop[i] = cat8(lds16(sw + swz64(row, 2 * q)), lds16(sw + swz64(row, 2 * q + 1)));
         }
 #pragma unroll
@@ -463,9 +483,9 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
         }
     };
 
-    v16f acc[4][kJX];
+    v16f acc[kNI][kJX];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int jx = 0; jx < kJX; ++jx)
 #pragma unroll
@@ -476,21 +496,21 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
     // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
     // stage kt (read one step earlier) run.
-    auto step = [&](int kt, const v8i (&cw)[4], const v8i (&ca)[kJX], v8i (&nw)[4], v8i (&na)[kJX]) {
+    auto step = [&](int kt, const v8i (&cw)[kNI], const v8i (&ca)[kJX], v8i (&nw)[kNI], v8i (&na)[kJX]) {
         wait_vmcnt<(kRing - 3) * kLoads>();
         __syncthreads();
         issue(kt + kRing - 1);
         if (kt + 1 < nk) read_ops(kt + 1, nw, na);
         __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kNI; ++i)
 #pragma unroll
             for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
         __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
     };
 #pragma unroll
     for (int s = 0; s < kRing - 1; ++s) issue(s);
-    v8i w0[4], a0[kJX], w1[4], a1[kJX];
+    v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
     wait_vmcnt<(kRing - 2) * kLoads>();
     __syncthreads();
     read_ops(0, w0, a0);
@@ -512,10 +532,10 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
         // f32 output: each lane stores its four consecutive n of one m row straight from the
         // accumulators (16 bytes per lane; the output is twice the bf16 size, no LDS staging)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kNI; ++i)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int64_t nb = n0 + wn * 128 + i * 32 + gq * 8 + q * 4;
+                const int64_t nb = n0 + wn * (TN / 2) + i * 32 + gq * 8 + q * 4;
                 float sc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
@@ -530,10 +550,10 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     }
     __syncthreads();   // every wave is done reading the ring
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-            const int nl = wn * 128 + i * 32 + gq * 8;
+            const int nl = wn * (TN / 2) + i * 32 + gq * 8;
             const int64_t nb = n0 + nl + q * 4;
             float sc[4];
 #pragma unroll
@@ -549,10 +569,11 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
         }
     __syncthreads();
     const bool vec = (g.ld_out & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
-    const bool full = vec && m0 + TM <= g.m && n0 + kWT <= g.n;
+    const bool full = vec && m0 + TM <= g.m && n0 + TN <= g.n;
 #pragma unroll 4
-    for (int it = 0; it < TM * kWT / 8 / 512; ++it) {
+    for (int it = 0; it < TM * 256 / 8 / 512; ++it) {    // TM rows x 32 chunk slots of 16 bytes
         const int e = t + it * 512, ml = e >> 5, cn = e & 31;
+        if (cn >= TN / 8) continue;                          // past the tile's n extent
         uint4 v = lds16(smem + ml * 512 + ((cn ^ (ml & 15)) << 4));
         if (((ml >> 3) ^ (ml >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
         const int64_t mm = m0 + ml, nn = n0 + cn * 8;
@@ -598,22 +619,28 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
                out_f32};
     // buffer descriptors address the operands with 32-bit offsets
     const bool offsets_fit = n * k < (int64_t(1) << 31) && m * lda < (int64_t(1) << 31);
+    // m <= 640: a ring tile when it gives >= 160 workgroups; of 256 x 128 and 192 x 128 the one
+    // whose busiest CU pulls the fewest operand bytes, (workgroups per CU) x (tile n + tile m) x k
+    // (each CU's delivery rate is bounded by the requests it keeps in flight)
     const int64_t half_tiles = ((n + kWT - 1) / kWT) * ((m + 127) / 128);
-    if (m <= 640 && offsets_fit && half_tiles >= 160) {
-        tile256_kernel<128><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
+    const int64_t t192 = ((n + 191) / 192) * ((m + 127) / 128);
+    if (m <= 640 && offsets_fit && (half_tiles >= 160 || t192 >= 160)) {
+        const int64_t c256 = half_tiles >= 160 ? ((half_tiles + 255) / 256) * (256 + 128) : INT64_MAX;
+        const int64_t c192 = t192 >= 160 ? ((t192 + 255) / 256) * (192 + 128) : INT64_MAX;
+        if (c192 < c256) {
+            tile256_kernel<192, 128><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
+            return check_launch("gemm (192 x 128)");
+        }
+        tile256_kernel<256, 128><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 128)");
     }
-    if (m <= 640 && offsets_fit) {
-        const int64_t big_tiles = ((n + 191) / 192) * ((m + 127) / 128);
-        if (big_tiles >= 160)
-            launch_panel<128, 48>(g, st);
-        else
-            launch_panel<64, 32>(g, st);
+    if (m <= 640 && offsets_fit) {   // too few ring tiles to fill the chip
+        launch_panel<64, 32>(g, st);
         return check_launch("gemm (panel)");
     }
     const int64_t wide_tiles = ((n + kWT - 1) / kWT) * ((m + kWT - 1) / kWT);
     if (offsets_fit && wide_tiles >= 160) {
-        tile256_kernel<256><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
+        tile256_kernel<256, 256><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 256)");
     }
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));

@@ -66,14 +66,15 @@ def test_linear_sweep_shapes(nhm, m, n, k):
     _check(nhm, a, w, ws, sa)
 
 
-# m <= 16: GEMV; m <= 640: the 256 x 128 ring kernel when it has >= 160 tiles (500 x 10000
-# x 2672: 160 tiles, ragged m, n and k), else the panel kernel (128 x 192 tiles when they give
-# >= 160 workgroups -- 384 x 10300 x 2608 -- else 64 x 128); larger m: the 256 x 256 tile kernel when it has >= 160
-# tiles (the last two shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
+# m <= 16: GEMV; m <= 640: a ring kernel when it has >= 160 tiles -- 192 x 128 (384 x 10300
+# x 2608: 162 tiles; 500 x 10000 x 2672: ragged m, n and k) or 256 x 128, whichever puts fewer
+# operand bytes on a CU (600 x 10304: 205 tiles of 256 x 128 against 270 of 192 x 128) --
+# else the 64 x 128 panel kernel; larger m: the 256 x 256 tile kernel
+# when it has >= 160 tiles (the last two shapes), else the 128 x 128 one. The ragged shapes cut every kind of tile edge (2600 x 4100
 # x 272: partial m and n tiles, n % 8 != 0, k ending inside a 64-byte ring stage).
 @pytest.mark.parametrize("m,n,k", [(1, 64, 128), (3, 100, 48), (16, 200, 272), (17, 130, 256),
                                    (130, 70, 144), (5, 1000, 4096), (200, 10304, 2688),
-                                   (384, 10300, 2608), (500, 10000, 2672), (641, 130, 256), (700, 520, 272),
+                                   (384, 10300, 2608), (500, 10000, 2672), (600, 10304, 2688), (641, 130, 256), (700, 520, 272),
                                    (2600, 4100, 272), (1030, 10304, 2688),
                                    (3, 520, 12288), (2, 130, 16384)])     # the GEMV's 16-wave variants
 def test_linear_ragged(nhm, m, n, k):
@@ -116,7 +117,7 @@ def test_linear_strided_output_wide_tiles(nhm, ld_pad):
 
 
 # f32 output (the D = f32 plan): the unrounded result, through every dispatch path -- GEMV
-# (m <= 16), the 256 x 128 ring tile (500 x 10000), the panel kernel (384 and 200 x 10304,
+# (m <= 16), the 192 x 128 ring tile (384 x 10300, 500 x 10000), the panel kernel (200 x 10304,
 # 130 x 70), the
 # 128 x 128 tile (641 x 130, 1030 x 2688) and the 256 x 256 tile (2600 x 4100 x 272, ragged).
 # Bound: the f32 accumulation term of the bf16 test without the bf16 rounding,
