@@ -6,8 +6,9 @@
 // each operand and 32 bytes of the 128-deep k-step; any assignment of k to lanes
 // works as long as both operands use the same one.
 //
-// Two kernels:
-//  * panel kernel (m up to a few hundred rows): a workgroup owns a BN-row panel of
+// Three kernels:
+//  * panel kernel (m up to 640 where the ring tiles are too few to fill the chip; 64 x 128
+//    tiles): a workgroup owns a BN-row panel of
 //    the weight and a BM-row tile of the activations. Each of its 4 waves streams
 //    its own WN weight rows straight from memory into MFMA registers, two k-steps
 //    ahead; only the activation tile, which all 4 waves share, is staged in LDS
@@ -16,13 +17,15 @@
 //    one XCD so the panel is fetched into that XCD's L2 once. Loads go through
 //    buffer descriptors, whose range check returns zeros past the operand's end,
 //    so ragged edges and padded steps need no branches in the loop.
-//  * 256 x 256 and 256 x 128 tile kernels (enough tiles to fill the chip): both operand tiles
-//    stream into a five-stage LDS ring by direct-to-LDS buffer loads (no register
-//    round trip; the range check zero-fills ragged rows and k), eight waves of
-//    128 x 64 on the 32x32x64 MFMA read the operands of the next stage while the
-//    MFMAs of the current one run, and the bf16 result leaves through LDS so that
-//    every store writes whole output rows. The wide tile halves the operand bytes
-//    per MAC of a 128 x 128 tile, which is what bounds this GEMM on the L2 -> CU path.
+//  * ring tile kernel, 256 x 256, 256 x 128 or 192 x 128 (enough tiles to fill the chip):
+//    both operand tiles stream into an LDS ring of 64-byte k-slices (5 to 8 stages, as many
+//    as fit 160 KB) by direct-to-LDS buffer loads (no register round trip; the range check
+//    zero-fills ragged rows and k), eight waves on the 32x32x64 MFMA read the operands of
+//    the next stage while the MFMAs of the current one run, and the bf16 result leaves
+//    through LDS so that every store writes whole output rows. Each CU receives operands
+//    at a rate bounded by the requests it keeps in flight, so the operand bytes a CU must
+//    pull set the time: wide tiles (fewer bytes per MAC) at large m, and at m <= 640 the
+//    tile shape whose busiest CU pulls the fewest bytes.
 //  * 128 x 128 tile kernel (remaining shapes): both operands staged through
 //    double-buffered LDS, four waves of 64 x 64.
 #include <stdint.h>
@@ -602,9 +605,9 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 }
 
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
-// 256 x 128 ring kernel (164 tiles) takes in_proj to 28.8 us from the panel kernel's 30.4
-// (its deeper, register-free prefetch); the panel kernel with 128 x 192 tiles took it from
-// 37 to 33 us; where those
+// 192 x 128 ring tile (216 workgroups of 860 KB) takes in_proj to 25.4 us, against 28.6 for
+// 256 x 128 (164 of 1 MB) and 30.4 for a 128 x 192 panel kernel (two k-steps of register
+// prefetch); earlier panel versions took it from 37 to 33 us; where those
 // tiles give too few workgroups to fill the chip (out_proj: 56), 64 x 128 tiles
 // (168 workgroups) take it from 34 to 21 us. The 256 x 256 kernel leads from about
 // 160 of its tiles (m = 1024 for in_proj, m = 4096 for out_proj: 45 vs 54 us and
