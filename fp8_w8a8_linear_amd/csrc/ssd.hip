@@ -43,14 +43,16 @@ __device__ __forceinline__ uint16_t bits(__bf16 v) { return __builtin_bit_cast(u
 // over the chunk, in s_dt / s_cs, for the raw value u that thread s < Q loaded; also
 // stored for the other kernels. Threads 0..127 are waves 0 and 1: each scans its 64
 // values with lane shuffles, then wave 1 adds wave 0's total. Ends with a barrier.
-__device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, int L, float u, float* s_dt,
-                                            float* s_cs) {
+// u: the token's raw dt (bf16 widened); dt_bias, a_log: the head's parameters, loaded by the
+// caller ahead of its bulk loads.
+__device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, int L, float u, float dt_bias,
+                                            float a_log, float* s_dt, float* s_cs) {
     const int t = threadIdx.x, lane = t & 63;
     __shared__ float s_w0;
     float dt = 0.f, v = 0.f;
     if (t < kQ) {
-        dt = t < L ? softplus(u + a.dt_bias[h]) : 0.f;
-        v = dt * -__expf(a.A_log[h]);
+        dt = t < L ? softplus(u + dt_bias) : 0.f;
+        v = dt * -__expf(a_log);
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float w = __shfl_up(v, o, 64);
@@ -103,7 +105,13 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_state_kernel(const PrefillArg
     __shared__ __attribute__((aligned(16))) uint16_t s_bt[kDS * kLd];   // B^T [n][s]
 
     // All global loads first (rows past the chunk's end read its last row and are zeroed
-    // when stored), then the decay scan, then the LDS stores.
+    // when stored), then the decay scan, then the LDS stores. The scan's dt goes out first:
+    // loads complete in issue order, so the scan waits for it alone and runs while the
+    // staging loads are in flight.
+    const int tr = t < L ? t : L - 1;
+    const float u = bf16_to_f32(a.zxbcdt[(tok0 + tr) * a.d_in_proj + a.dt_off + h]);
+    const float dt_bias = a.dt_bias[h], a_log = a.A_log[h];
+    asm volatile("" ::: "memory");
     constexpr int kXI = kQ * (kHP / 8) / kThreads, kBI = kQ * (kDS / 8) / kThreads;
     uint4 xv[kXI], bv[kBI];
 #pragma unroll
@@ -116,9 +124,7 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_state_kernel(const PrefillArg
         const int e = t + i * kThreads, s = e & (kQ - 1), n8 = e >> 7;
         bv[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (s < L ? s : L - 1)) * a.conv_dim + a.b_off + g * kDS + n8 * 8);
     }
-    const int tr = t < L ? t : L - 1;
-    const float u = bf16_to_f32(a.zxbcdt[(tok0 + tr) * a.d_in_proj + a.dt_off + h]);
-    chunk_decay(a, c, h, L, u, s_dt, s_cs);
+    chunk_decay(a, c, h, L, u, dt_bias, a_log, s_dt, s_cs);
     const float cs_end = s_cs[L - 1];
     if (t < kQ) s_w[t] = t < L ? __expf(cs_end - s_cs[t]) * s_dt[t] : 0.f;
 #pragma unroll
@@ -219,6 +225,13 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
     // LDS store (a load-store loop would pay one memory latency per iteration). Rows past
     // the chunk's end are read from its last row (always in bounds) and zeroed.
     constexpr int kXI = kQ * (kHP / 8) / kThreads, kBI = kQ * (kDS / 8) / kThreads, kHI = kHP * kDS / 4 / kThreads;
+    // the small cumulative-decay and dt rows first (loads complete in issue order: the staging
+    // below then waits for each operand as it arrives, not for everything)
+    const float* cs_in = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
+    const float* dt_in = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
+    const int tq = t & (kQ - 1);
+    const float csv = cs_in[tq], dtv = dt_in[tq];
+    asm volatile("" ::: "memory");
     uint4 xv[kXI], bv[kBI];
     float4 hv[kHI];
 #pragma unroll
@@ -238,14 +251,6 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
     bf16x8 cop[kDS / 32];                             // C[t][k-step]
 #pragma unroll
     for (int kn = 0; kn < kDS / 32; ++kn) cop[kn] = *reinterpret_cast<const bf16x8*>(crow + kn * 32);
-    const float* cs_in = a.chunk_cs + ((int64_t)c * a.n_heads + h) * kQ;
-    const float* dt_in = a.chunk_dt + ((int64_t)c * a.n_heads + h) * kQ;
-    float csv = 0.f, dtv = 0.f;
-    if (t < kQ) {
-        csv = cs_in[t];
-        dtv = dt_in[t];
-    }
-
     if (t < kQ) {
         s_cs[t] = csv;
         s_dt[t] = dtv;
