@@ -90,6 +90,17 @@ def test_linear_prequantized_input(nhm, m):
     _check(nhm, a, w, ws, sa, via_e4m3=True)
 
 
+# A per-tensor weight scale (one scalar per projection) is the per-channel vector with every
+# entry equal: through the GEMV, the 64 x 128 panel, the 192 x 128 ring and the 256 x 256 tile.
+@pytest.mark.parametrize("m,n,k", [(8, 10304, 2688), (200, 10304, 2688), (512, 10304, 2688),
+                                   (2600, 4100, 272)])
+def test_linear_per_tensor_weight_scale(nhm, m, n, k):
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=10, per_tensor=True)
+    assert np.all(ws == ws[0])
+    _check(nhm, a, w, ws, sa)
+
+
 # ld_pad 13 makes the row stride odd: the kernels fall back from 8-byte stores
 @pytest.mark.parametrize("m", [2, 100, 700])
 @pytest.mark.parametrize("ld_pad", [12, 13])

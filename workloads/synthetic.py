@@ -46,10 +46,13 @@ def bf16_bits(a):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def e4m3_weight(g, n, k, std=0.02):
-    """W ~ N(0, std) [n, k]; per-output-channel scale amax/448; codes of W/scale."""
+def e4m3_weight(g, n, k, std=0.02, per_tensor=False):
+    """W ~ N(0, std) [n, k]; per-output-channel scale amax/448 (per_tensor: one scale, the
+    whole tensor's amax/448, repeated for every channel); codes of W/scale."""
     w = g.standard_normal((n, k), dtype=np.float32) * np.float32(std)
     amax = np.abs(w).max(axis=1)
+    if per_tensor:
+        amax = np.full_like(amax, amax.max() if amax.size else 0.0)
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     q = torch.from_numpy(w / scale[:, None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).numpy().copy(), scale
@@ -101,8 +104,9 @@ def slots(workload, count, S):
     return rng(workload, "slot").choice(S, size=count, replace=False).astype(np.int32)
 
 
-def linear_case(m, n, k, extra=0):
-    """One W8A8 linear case: bf16 activations ~ N(0,1) [m,k]; weights as for a block."""
+def linear_case(m, n, k, extra=0, per_tensor=False):
+    """One W8A8 linear case: bf16 activations ~ N(0,1) [m,k]; weights as for a block
+    (per_tensor: one weight scale for the whole tensor)."""
     a = bf16_bits(rng(1, "act", m * 100003 + n, extra).standard_normal((m, k), dtype=np.float32))
-    w, ws = e4m3_weight(rng(1, "weight", n * 100003 + k, extra), n, k)
+    w, ws = e4m3_weight(rng(1, "weight", n * 100003 + k, extra), n, k, per_tensor=per_tensor)
     return a, w, ws, np.array([4.0 / 448.0], dtype=np.float32)
