@@ -130,15 +130,14 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
 }
 
 // The weight-streaming GEMV serves m <= 16 (k up to 16384, weights under 2 GiB: its buffer
-// descriptors take 32-bit offsets); the tiled GEMM the rest. A decode step always takes
-// the GEMV, which carries the conv epilogue, and reports geometries beyond its limits.
+// descriptors take 32-bit offsets); the tiled GEMM the rest.
 static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
 
 // One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
-                          int64_t ld_out, const ConvEpilogue* conv, hipStream_t st, float* out_f32 = nullptr) {
-    if (conv || use_gemv(m, w.n, w.k))
-        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, conv, st, out_f32);
+                          int64_t ld_out, hipStream_t st, float* out_f32 = nullptr) {
+    if (use_gemv(m, w.n, w.k))
+        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
     return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
 }
 
@@ -265,8 +264,8 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
         aq = q;
         lda = w->k;
     }
-    if (out_type == NHM_F32) return project(aq, lda, m, *w, nullptr, ld_out, nullptr, st, static_cast<float*>(out));
-    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, nullptr, st);
+    if (out_type == NHM_F32) return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out));
+    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, st);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
@@ -331,9 +330,7 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     if ((s = check_launch("decode quant")) != NHM_OK) return s;
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        ConvEpilogue ce{slot_idx + r0, conv_pool, p->conv_w, p->conv_b, xc + (int64_t)r0 * l.conv_dim, l.xbc_off,
-                        l.conv_dim};
-        s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, &ce, st);
+        s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, st);
         if (s != NHM_OK) return s;
     }
     DecodeSsmArgs da;
@@ -342,6 +339,9 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     da.ssm_pool_bf16 = ssm_type == NHM_BF16 ? static_cast<uint16_t*>(ssm_pool) : nullptr;
     da.zxbcdt = zx;
     da.xbc_conv = xc;
+    da.conv_pool = conv_pool;
+    da.conv_w = p->conv_w;
+    da.conv_b = p->conv_b;
     da.A_log = p->A_log;
     da.D = p->D;
     da.dt_bias = p->dt_bias;
@@ -351,16 +351,24 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     da.d_in_proj = l.d_in_proj;
     da.conv_dim = l.conv_dim;
     da.d_inner = l.d_inner;
+    da.xbc_off = l.xbc_off;
     da.dt_off = l.dt_off;
     da.b_off = l.b_off;
     da.c_off = l.c_off;
     if ((s = launch_decode_ssm(da, batch, st)) != NHM_OK) return s;
     GnormArgs ga{batch, p->g.n_groups, l.d_inner, l.d_in_proj, l.z_off, p->g.rms_eps, da.y, zx, p->norm_w,
                  p->out_proj.a_scale, reinterpret_cast<uint16_t*>(wsb + w.pub.norm), q_out};
+    ga.slot_idx = slot_idx;   // the B and C conv windows are shifted here (see DecodeSsmArgs)
+    ga.conv_pool = conv_pool;
+    ga.conv_dim = l.conv_dim;
+    ga.xbc_off = l.xbc_off;
+    ga.b_off = l.b_off;
+    ga.c_off = l.c_off;
+    ga.d_state = p->g.d_state;
     if ((s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, nullptr, st);
+        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, st);
         if (s != NHM_OK) return s;
     }
     return NHM_OK;
@@ -413,7 +421,7 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     if (n_tokens > 0) {
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
-        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, nullptr, st)) != NHM_OK) return s;
+        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, st)) != NHM_OK) return s;
     }
     PrefillArgs a;
     // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every later
@@ -467,7 +475,7 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     a.q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
     if ((s = launch_prefill_mid(a, st)) != NHM_OK) return s;
     if (n_tokens > 0)
-        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, nullptr, st);
+        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, st);
     return NHM_OK;
 }
 

@@ -26,13 +26,12 @@ struct GemvArgs {
     uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
     float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
     int ksteps;
-    int rows;                                       // features per workgroup: 16, or a multiple of 4 below
-    ConvEpilogue conv;
+    int rows;                                       // features per workgroup, a multiple of 4 up to 16 x kTiles
 };
 
 constexpr int kStreamAux = 2;   // non-temporal: weight rows are read exactly once
 
-template <int kWaves, int kSteps, bool kConv, int kTiles>
+template <int kWaves, int kSteps, int kTiles>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves - 1][kTiles][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -49,33 +48,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     // Everything up to the MFMAs is straight-line code: loads past the operands go to an
     // out-of-range buffer offset (zeros) and indexes are clamped, so the compiler can wait
     // for each k-step's loads alone instead of for all outstanding loads at a branch join.
-    // First the small operands of the epilogue (so that waiting for them later does not
-    // wait for the weight stream), then the weight stream, k-step by k-step.
+    // First the scales of the epilogue (so that waiting for them later does not wait for the
+    // weight stream), then the weight stream, k-step by k-step.
     const float sa = *g.a_scale;
     float sc[kTiles][4];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[nbase[t] + r < g.n ? nbase[t] + r : g.n - 1];
-    int slot = -1;
-    int64_t ch[kTiles];
-    uint4 cw0[kTiles], cw1[kTiles];
-    uint2 cb[kTiles];
-    if constexpr (kConv) {
-        const ConvEpilogue& c = g.conv;
-        slot = c.slot_idx[col < g.m ? col : 0];
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            ch[t] = nbase[t] - c.xbc_off;
-            const int64_t chc = ch[t] < 0 ? 0 : (ch[t] > c.conv_dim - 4 ? c.conv_dim - 4 : ch[t]);
-            cw0[t] = *reinterpret_cast<const uint4*>(c.conv_w + chc * 4);      // taps of channels ch, ch+1
-            cw1[t] = *reinterpret_cast<const uint4*>(c.conv_w + chc * 4 + 8);  // channels ch+2, ch+3
-            cb[t] = *reinterpret_cast<const uint2*>(c.conv_b + chc);
-            // features past this workgroup's end belong to the next one (whole 4-feature groups:
-            // rows per workgroup, xbc_off and conv_dim are multiples of 4)
-            if (ch[t] >= c.conv_dim || col >= g.m || nbase[t] >= nend) ch[t] = -1;
-        }
-    }
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
@@ -96,19 +76,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
             wa[i][t] = bload32<kStreamAux>(wrs, kb < g.k ? wrow[t] + kb : kGemvOut,
                                            kb + 16 < g.k ? wrow[t] + kb + 16 : kGemvOut);
         xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
-    }
-    // the carried conv window of this token's sequence (slot row 0 stands in for a padded row)
-    uint2 w0[kTiles], w1[kTiles], w2[kTiles];
-    if constexpr (kConv) {
-        const ConvEpilogue& c = g.conv;
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const int64_t chc = ch[t] < 0 ? 0 : ch[t];
-            const uint16_t* win = c.conv_pool + (int64_t)(slot < 0 ? 0 : slot) * 3 * c.conv_dim + chc;
-            w0[t] = *reinterpret_cast<const uint2*>(win);
-            w1[t] = *reinterpret_cast<const uint2*>(win + c.conv_dim);
-            w2[t] = *reinterpret_cast<const uint2*>(win + 2 * c.conv_dim);
-        }
     }
     // keep every load above issued before the first MFMA (the scheduler would otherwise sink
     // later steps' loads below earlier steps' MFMAs, serialising the stream)
@@ -146,11 +113,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
     // acc[t][r] = D[feature nbase[t] + r][token col]
     if (col >= g.m) return;
-    if (g.out_f32) {   // (never with the conv epilogue)
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const int64_t nb = nbase[t];
-            if (nb >= nend) break;   // row tiles are in feature order
+    for (int t = 0; t < kTiles; ++t) {
+        const int64_t nb = nbase[t];
+        if (nb >= nend) break;   // row tiles are in feature order
+        if (g.out_f32) {
             float* of = g.out_f32 + (int64_t)col * g.ld_out + nb;
             if (g.vec_out && nb + 3 < nend) {
                 *reinterpret_cast<float4*>(of) =
@@ -159,85 +126,32 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
                 for (int r = 0; r < 4; ++r)
                     if (nb + r < nend) of[r] = acc[t][r] * sc[t][r];
             }
+            continue;
         }
-        return;
-    }
-    // All arithmetic before the first store: a wait for the conv window (loads and stores
-    // share one in-order counter) would otherwise also wait for the acknowledgement of every
-    // store issued before it.
-    uint32_t hb[kTiles][4];
+        uint32_t hb[4];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[t][r] = f32_to_bf16(acc[t][r] * sc[t][r]);
-    uint32_t ob[kTiles][4];
-    if constexpr (kConv) {
-        // causal depthwise conv (width 4) + SiLU on the xBC features
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const uint32_t u0[4] = {w0[t].x & 0xffffu, w0[t].x >> 16, w0[t].y & 0xffffu, w0[t].y >> 16};
-            const uint32_t u1[4] = {w1[t].x & 0xffffu, w1[t].x >> 16, w1[t].y & 0xffffu, w1[t].y >> 16};
-            const uint32_t u2[4] = {w2[t].x & 0xffffu, w2[t].x >> 16, w2[t].y & 0xffffu, w2[t].y >> 16};
-            const uint32_t wt[8] = {cw0[t].x, cw0[t].y, cw0[t].z, cw0[t].w, cw1[t].x, cw1[t].y, cw1[t].z, cw1[t].w};
-            const uint32_t bb[4] = {cb[t].x & 0xffffu, cb[t].x >> 16, cb[t].y & 0xffffu, cb[t].y >> 16};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // taps of channel ch+r: bf16 [4] = words wt[2r] (taps 0,1) and wt[2r+1] (taps 2,3)
-                float pre = bf16_to_f32(bb[r]);
-                pre = fmaf(bf16_to_f32(wt[2 * r] & 0xffffu), bf16_to_f32(u0[r]), pre);
-                pre = fmaf(bf16_to_f32(wt[2 * r] >> 16), bf16_to_f32(u1[r]), pre);
-                pre = fmaf(bf16_to_f32(wt[2 * r + 1] & 0xffffu), bf16_to_f32(u2[r]), pre);
-                pre = fmaf(bf16_to_f32(wt[2 * r + 1] >> 16), bf16_to_f32(hb[t][r]), pre);
-                ob[t][r] = f32_to_bf16(silu(pre));
-            }
-        }
-        // materialise the results here (the compiler would sink them into the store loop)
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t)
-            asm volatile("" ::"v"(ob[t][0]), "v"(ob[t][1]), "v"(ob[t][2]), "v"(ob[t][3]) : "memory");
-    }
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-        const int64_t nb = nbase[t];
-        if (nb >= nend) break;   // row tiles are in feature order
+        for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[t][r] * sc[t][r]);
         uint16_t* o = g.out + (int64_t)col * g.ld_out + nb;
         if (g.vec_out && nb + 3 < nend) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(hb[t][0] | (hb[t][1] << 16), hb[t][2] | (hb[t][3] << 16));
+            *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         } else {
             for (int r = 0; r < 4; ++r)
-                if (nb + r < nend) o[r] = (uint16_t)hb[t][r];
-        }
-        if constexpr (kConv) {
-            // the conv output and the window shifted in place (a padded row: zero output, no window)
-            const ConvEpilogue& c = g.conv;
-            if (ch[t] < 0) continue;
-            uint16_t* xo = c.xbc_conv + (int64_t)col * c.conv_dim + ch[t];
-            if (slot < 0) {
-                *reinterpret_cast<uint2*>(xo) = make_uint2(0u, 0u);
-                continue;
-            }
-            uint16_t* win = c.conv_pool + (int64_t)slot * 3 * c.conv_dim + ch[t];
-            *reinterpret_cast<uint2*>(xo) = make_uint2(ob[t][0] | (ob[t][1] << 16), ob[t][2] | (ob[t][3] << 16));
-            *reinterpret_cast<uint2*>(win) = w1[t];
-            *reinterpret_cast<uint2*>(win + c.conv_dim) = w2[t];
-            *reinterpret_cast<uint2*>(win + 2 * c.conv_dim) =
-                make_uint2(hb[t][0] | (hb[t][1] << 16), hb[t][2] | (hb[t][3] << 16));
+                if (nb + r < nend) o[r] = (uint16_t)hb[r];
         }
     }
 }
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
-                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, hipStream_t st, float* out_f32) {
+                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
+                       float* out_f32) {
     GemvArgs g;
     g.a = a; g.lda = lda; g.m = m;
     g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
     g.out = out; g.ld_out = ld_out;
-    g.out_f32 = conv ? nullptr : out_f32;
+    g.out_f32 = out_f32;
     g.vec_out = out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
                         : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
     g.ksteps = (int)((k + 127) / 128);
-    g.conv = conv ? *conv : ConvEpilogue{};
     if (g.ksteps > 16 * kGemvMaxSteps)
         return fail(NHM_ERR_UNSUPPORTED, "gemv: k %lld exceeds %d", (long long)k, 16 * 128 * kGemvMaxSteps);
     if (n * k >= (int64_t(1) << 31) || (int64_t)m * lda >= (int64_t(1) << 31))
@@ -262,11 +176,7 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     }
     const int tiles = (g.rows + 15) / 16;
     const dim3 grid((unsigned)((n + g.rows - 1) / g.rows));
-#define NHM_GEMV_LAUNCH(W, S, T)                                                  \
-    do {                                                                          \
-        if (conv) gemv_kernel<W, S, true, T><<<grid, dim3(W * 64), 0, st>>>(g);  \
-        else gemv_kernel<W, S, false, T><<<grid, dim3(W * 64), 0, st>>>(g);      \
-    } while (0)
+#define NHM_GEMV_LAUNCH(W, S, T) gemv_kernel<W, S, T><<<grid, dim3(W * 64), 0, st>>>(g)
 #define NHM_GEMV_STEPS(W, T)                         \
     do {                                             \
         if (steps == 2) NHM_GEMV_LAUNCH(W, 2, T);    \

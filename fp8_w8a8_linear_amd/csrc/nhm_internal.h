@@ -27,26 +27,12 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
 
 // ---- weight-streaming GEMV for m <= 16 (gemv.hip)
 
-// Epilogue of the in_proj GEMV inside a decode step: besides storing the bf16
-// projection, runs the causal conv + SiLU on the xBC columns and shifts the
-// carried conv window of each sequence in place.
-struct ConvEpilogue {
-    const int32_t* slot_idx;   // [m]
-    uint16_t* conv_pool;       // [S, W-1, conv_dim]
-    const uint16_t* conv_w;    // [conv_dim, W]
-    const uint16_t* conv_b;    // [conv_dim]
-    uint16_t* xbc_conv;        // [m, conv_dim]
-    int32_t xbc_off;           // first xBC column of the projection
-    int32_t conv_dim;
-};
-
-// out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda].
-// conv == nullptr: plain store to out[m * ld_out + n]; otherwise also the conv epilogue
-// (which needs the xBC range to start on a multiple of 32 features). out_f32 (without
-// conv): the unrounded f32 result goes to out_f32[m * ld_out + n] instead of out.
+// out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda], stored to
+// out[m * ld_out + n]; with out_f32 the unrounded f32 result goes to out_f32[m * ld_out + n]
+// instead.
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
-                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       const ConvEpilogue* conv, hipStream_t st, float* out_f32 = nullptr);
+                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
+                       float* out_f32 = nullptr);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
@@ -54,17 +40,24 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
                        hipStream_t st, float* out_f32 = nullptr);
 
 // ---- decode SSM state update (decode.hip)
+// The kernel also runs the causal conv + SiLU of the channels it reads (the head's x, the
+// group's B and C) from the pre-conv projection and the carried window, stores them to
+// xbc_conv, and shifts the windows of the head's x channels; the B and C channels' windows
+// (read by every head of the group) are shifted by the gated-norm kernel that follows.
 struct DecodeSsmArgs {
     const int32_t* slot_idx;
     float* ssm_pool;           // f32 state pool, or nullptr with ssm_pool_bf16
     uint16_t* ssm_pool_bf16;   // bf16 state pool (widened on load, rounded on store), or nullptr
     const uint16_t* zxbcdt;    // [m, d_in_proj]
-    const uint16_t* xbc_conv;  // [m, conv_dim]
+    uint16_t* xbc_conv;        // [m, conv_dim] conv + SiLU output
+    uint16_t* conv_pool;       // [S, W-1, conv_dim]
+    const uint16_t* conv_w;    // [conv_dim, W]
+    const uint16_t* conv_b;    // [conv_dim]
     const float* A_log;
     const float* D;
     const float* dt_bias;
     uint16_t* y;               // [m, d_inner]
-    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, dt_off, b_off, c_off;
+    int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, xbc_off, dt_off, b_off, c_off;
 };
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st);
 
@@ -79,6 +72,11 @@ struct GnormArgs {
     const float* out_a_scale;  // [1]
     uint16_t* norm;            // [T, d_inner] bf16 norm output (nullptr: not kept)
     uint8_t* q_out;            // [T, d_inner]
+    // decode: shift the B and C channels' conv windows of each token's slot (slot_idx ==
+    // nullptr: none). Row 2 takes the pre-conv value from zxbcdt.
+    const int32_t* slot_idx = nullptr;
+    uint16_t* conv_pool = nullptr;   // [S, W-1, conv_dim]
+    int32_t conv_dim = 0, xbc_off = 0, b_off = 0, c_off = 0, d_state = 0;
 };
 nhm_status launch_gnorm_quant(const GnormArgs& a, hipStream_t st);
 

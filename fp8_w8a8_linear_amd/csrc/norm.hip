@@ -24,6 +24,23 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
     const uint16_t* yr = a.y + tok * a.d_inner + (int64_t)g * gw;
     const uint16_t* zr = a.zxbcdt + tok * a.d_in_proj + a.z_off + (int64_t)g * gw;
     const float so = *a.out_a_scale;
+    // decode: this token's slot's conv windows of group g's B (lanes 0-31) and C (32-63)
+    // channels, four per lane, shifted by one row (the decode state kernel, which reads them,
+    // has finished; the x channels' windows it shifts itself). Loads go out with y and z.
+    int wslot = -1;
+    int64_t wc = 0;
+    uint2 r1{}, r2{};
+    uint32_t cur[4] = {0u, 0u, 0u, 0u};
+    if (a.slot_idx) {
+        wslot = a.slot_idx[tok];
+        wc = lane < 32 ? a.b_off + (int64_t)g * a.d_state + 4 * lane : a.c_off + (int64_t)g * a.d_state + 4 * (lane - 32);
+        const uint16_t* win = a.conv_pool + (int64_t)(wslot < 0 ? 0 : wslot) * 3 * a.conv_dim + wc;
+        r1 = *reinterpret_cast<const uint2*>(win + a.conv_dim);
+        r2 = *reinterpret_cast<const uint2*>(win + 2 * a.conv_dim);
+        const uint16_t* pc = a.zxbcdt + tok * a.d_in_proj + a.xbc_off + wc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] = pc[j];
+    }
     // emit(c, v, r, nw): nw holds norm_w[c .. c + 7] (loaded with y and z where possible)
     auto emit = [&](int c, const float (&v)[8], float r, const uint4 nw) {
         const bool fast = fast_scale(so);    // the quant's reciprocal form (exact; see quant_bf16x8_fast)
@@ -95,6 +112,12 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const GnormArgs a) {
             for (int j = 0; j < 8; ++j) v[j] = y[j] * silu(z[j]);
             emit(c, v, r, *reinterpret_cast<const uint4*>(a.norm_w + (int64_t)g * gw + c));
         }
+    }
+    if (wslot >= 0) {
+        uint16_t* win = a.conv_pool + (int64_t)wslot * 3 * a.conv_dim + wc;
+        *reinterpret_cast<uint2*>(win) = r1;
+        *reinterpret_cast<uint2*>(win + a.conv_dim) = r2;
+        *reinterpret_cast<uint2*>(win + 2 * a.conv_dim) = make_uint2(cur[0] | (cur[1] << 16), cur[2] | (cur[3] << 16));
     }
 }
 
