@@ -128,7 +128,7 @@ def test_decode_one_block_one_token(nhm, block0):
                                            (64, None, 64)])        # the whole 64-slot pool in one call
 def test_decode_batch(nhm, block0, B, slot_list, S):
     from oracle import mixer_decode
-    from tests.gpu_util import upload_params
+    from tests.gpu_util import upload_params, ws_region
     from workloads import conv_pool, hidden, slots, ssm_pool
     h = hidden(2, B, extra=B)
     sl = np.array(slot_list, np.int32) if slot_list else slots(2, B, S)
@@ -137,6 +137,10 @@ def test_decode_batch(nhm, block0, B, slot_list, S):
     out, spg, cpg, ws, lay = _gpu_decode(nhm, pd, h, sl, sp, cp)
     spr, cpr = sp.copy(), cp.copy()
     ref, res = mixer_decode(block0, h, sl, spr, cpr)
+    # a1: the in_proj input codes kept in the workspace (quantized inside the GEMV launches of
+    # up to 16 rows each), every row, padded ones too
+    q_in = ws_region(ws, lay["q_in"], B * H, np.uint8).reshape(B, H)
+    assert np.array_equal(q_in, res["q_in"].reshape(B, H))
     live = [b for b in range(B) if sl[b] >= 0]
     m = _parity(out, ws, lay, live, ref, res["norm"][live], res["q_out"][live], block0)
     pad = [b for b in range(B) if sl[b] < 0]
