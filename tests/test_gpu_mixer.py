@@ -491,3 +491,79 @@ def test_prefill_ragged_15360_23_blocks(nhm):
                 failures.append(f"layer {layer} sequence {i} window")
         print(f"layer {layer} sequences {seqs} (rows {rows[0]}..{rows[-1]}): {m}, state rel l2 {states}")
     assert not failures, "; ".join(failures)
+
+
+# Another geometry: hidden 256, 8 heads of 64 in 2 groups (4 heads per group), so the B and C
+# channels sit at other offsets, the group's B/C windows are shared by 4 heads instead of 8,
+# and the projections take other dispatch shapes (in_proj 1544 x 256, out_proj 256 x 512).
+SMALL = dict(hidden=256, n_heads=8, head_dim=64, d_state=128, n_groups=2, conv_width=4, rms_eps=1e-5)
+
+
+def _small_parity(out, ws, lay, rows, T, ref, ref_norm, ref_q, p):
+    from tests.gpu_util import block_parity, ws_region
+    inner = SMALL["n_heads"] * SMALL["head_dim"]
+    q = ws_region(ws, lay["q_out"], T * inner, np.uint8).reshape(T, inner)[rows]
+    nrm = ws_region(ws, lay["norm"], T * inner, np.uint16).reshape(T, inner)[rows]
+    return block_parity(out[rows], q, nrm, ref[rows], ref_norm, ref_q, p)
+
+
+def test_decode_small_geometry(nhm):
+    """Decode at hidden 256, 8 heads in 2 groups, with a padded row."""
+    from oracle import mixer_decode
+    from tests.gpu_util import dev, host, upload_params, ws_region, zeros_ws
+    from workloads import block_params, conv_pool, hidden, ssm_pool
+    g, S, B = SMALL, 12, 6
+    p = block_params(5, 0, g)
+    h = hidden(5, B, g)
+    sl = np.array([3, 0, -1, 11, 7, 5], np.int32)
+    sp, cp = ssm_pool(5, 0, S, g=g), conv_pool(5, 0, S, g=g)
+    pd = upload_params(p, g)
+    lay = nhm.decode_ws_layout(B, g)
+    ws = zeros_ws(lay["total"])
+    spd, cpd = dev(sp), dev(cp)
+    out = torch.empty((B, g["hidden"]), dtype=torch.int16, device="cuda")
+    nhm.mixer_decode(pd, dev(h), dev(sl), spd, cpd, out, ws)
+    torch.cuda.synchronize()
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_decode(p, h, sl, spr, cpr, g=g)
+    q_in = ws_region(ws, lay["q_in"], B * g["hidden"], np.uint8).reshape(B, g["hidden"])
+    assert np.array_equal(q_in, res["q_in"].reshape(B, g["hidden"]))
+    o = host(out)
+    live = [b for b in range(B) if sl[b] >= 0]
+    m = _small_parity(o, ws, lay, live, B, ref, res["norm"][live], res["q_out"][live], p)
+    assert np.all(o[2] == 0)
+    touched = {int(s) for s in sl if s >= 0}
+    _check_states(host(spd), spr, sp, touched)
+    _check_windows(host(cpd), cpr, cp, touched)
+    print(f"decode small geometry: {m}")
+
+
+def test_prefill_small_geometry(nhm):
+    """Varlen prefill at hidden 256, 8 heads in 2 groups: a two-chunk sequence from a carried
+    state, a fresh one and a one-token continuation."""
+    from oracle import mixer_prefill
+    from tests.gpu_util import dev, host, upload_params, zeros_ws
+    from workloads import block_params, conv_pool, hidden, ssm_pool
+    g, S = SMALL, 10
+    lens, has_init = [130, 5, 1], [1, 0, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    p = block_params(6, 0, g)
+    h = hidden(6, T, g)
+    sl = np.array([4, 9, 0], np.int32)
+    sp, cp = ssm_pool(6, 0, S, g=g), conv_pool(6, 0, S, g=g)
+    pd = upload_params(p, g)
+    lay = nhm.prefill_ws_layout(T, len(lens), g=g)
+    ws = zeros_ws(lay["total"])
+    spd, cpd = dev(sp), dev(cp)
+    out = torch.empty((T, g["hidden"]), dtype=torch.int16, device="cuda")
+    nhm.mixer_prefill(pd, dev(h), dev(cu), dev(sl), dev(np.asarray(has_init, np.int32)), spd, cpd, out, ws)
+    torch.cuda.synchronize()
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_prefill(p, h, cu, sl, has_init, spr, cpr, g=g)
+    norm, q, _ = _prefill_refs(res, lens)
+    m = _small_parity(host(out), ws, lay, list(range(T)), T, ref, norm, q, p)
+    touched = {int(s) for s in sl}
+    _check_states(host(spd), spr, sp, touched)
+    _check_windows(host(cpd), cpr, cp, touched)
+    print(f"prefill small geometry {lens}: {m}")

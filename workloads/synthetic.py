@@ -58,19 +58,27 @@ def e4m3_weight(g, n, k, std=0.02, per_tensor=False):
     return q.view(torch.uint8).numpy().copy(), scale
 
 
+def _dims(g):
+    """(d_inner, conv_dim, d_in_proj) of a geometry."""
+    inner = g["n_heads"] * g["head_dim"]
+    conv_dim = inner + 2 * g["n_groups"] * g["d_state"]
+    return inner, conv_dim, inner + conv_dim + g["n_heads"]
+
+
 def block_params(workload, layer, g=GEOM):
     """All parameters of one mixer block, drawn in a fixed order from one stream."""
     r = rng(workload, "param", layer)
-    in_w, in_ws = e4m3_weight(r, D_IN_PROJ, g["hidden"])
-    out_w, out_ws = e4m3_weight(r, g["hidden"], INNER)
-    conv_w = bf16_bits(r.standard_normal((CONV_DIM, g["conv_width"]), dtype=np.float32) * np.float32(0.5))
-    conv_b = bf16_bits(r.standard_normal(CONV_DIM, dtype=np.float32) * np.float32(0.1))
+    inner, conv_dim, d_in_proj = _dims(g)
+    in_w, in_ws = e4m3_weight(r, d_in_proj, g["hidden"])
+    out_w, out_ws = e4m3_weight(r, g["hidden"], inner)
+    conv_w = bf16_bits(r.standard_normal((conv_dim, g["conv_width"]), dtype=np.float32) * np.float32(0.5))
+    conv_b = bf16_bits(r.standard_normal(conv_dim, dtype=np.float32) * np.float32(0.1))
     H = g["n_heads"]
     A_log = r.uniform(0.0, np.log(16.0), H).astype(np.float32)
     dtv = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), H))
     dt_bias = np.log(np.expm1(dtv)).astype(np.float32)     # inverse softplus of dtv
     D = (1.0 + 0.1 * r.standard_normal(H)).astype(np.float32)
-    norm_w = bf16_bits(1.0 + 0.1 * r.standard_normal(INNER).astype(np.float32))
+    norm_w = bf16_bits(1.0 + 0.1 * r.standard_normal(inner).astype(np.float32))
     a_scale = np.array([4.0 / 448.0], dtype=np.float32)
     return dict(in_w=in_w, in_w_scale=in_ws, in_a_scale=a_scale.copy(),
                 out_w=out_w, out_w_scale=out_ws, out_a_scale=a_scale.copy(),
@@ -93,7 +101,7 @@ def ssm_pool(workload, layer, S, zero=False, g=GEOM):
 
 def conv_pool(workload, layer, S, zero=False, g=GEOM):
     """bf16 conv window pool [S, W-1, conv_dim] ~ N(0, 1), oldest row first, or zeros."""
-    shp = (S, g["conv_width"] - 1, CONV_DIM)
+    shp = (S, g["conv_width"] - 1, _dims(g)[1])
     if zero:
         return np.zeros(shp, dtype=np.uint16)
     return bf16_bits(rng(workload, "conv", layer).standard_normal(shp, dtype=np.float32))
