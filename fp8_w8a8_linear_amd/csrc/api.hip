@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -78,13 +80,19 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
 // ---------------------------------------------------------------- workspace layouts
 
 // bytes of the e4m3 copy of a bf16 activation (the only workspace nhm_fp8_linear needs)
-static size_t linear_ws(int64_t m, int64_t k, nhm_dtype t) {
+// The linear's workspace: the activation codes of a bf16 input (required), then the split-k
+// partials of the shapes that take a split (optional: without them those shapes run unsplit).
+static size_t linear_codes_ws(int64_t m, int64_t k, nhm_dtype t) {
     return t == NHM_BF16 ? align_up((size_t)m * (size_t)k, 256) : 0;
+}
+static size_t linear_ws(int64_t m, int64_t n, int64_t k, nhm_dtype t) {
+    return linear_codes_ws(m, k, t) + align_up(gemm_part_bytes(m, n, k), 256);
 }
 
 struct MixerWs {
     nhm_ws_layout pub;
     size_t chunk_info, seq_chunk0, chunk_cs, chunk_dt, chunk_state;
+    size_t part, part_bytes;   // split-k partials of the projections (prefill)
     int max_chunks;
 };
 
@@ -125,6 +133,8 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     w.pub.y = take(Ts * l.d_inner * 2);
     w.pub.norm = take(Ts * l.d_inner * 2);
     w.pub.q_out = take(Ts * l.d_inner);
+    w.part_bytes = std::max(gemm_part_bytes(T, l.d_in_proj, g->hidden), gemm_part_bytes(T, g->hidden, l.d_inner));
+    w.part = take(w.part_bytes);
     w.pub.total = off;
     return w;
 }
@@ -134,11 +144,13 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
 static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
 
 // One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
+// part / part_bytes: scratch for the GEMM's split-k partials (nullptr: no split).
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
-                          int64_t ld_out, hipStream_t st, float* out_f32 = nullptr) {
+                          int64_t ld_out, hipStream_t st, float* out_f32 = nullptr, float* part = nullptr,
+                          size_t part_bytes = 0) {
     if (use_gemv(m, w.n, w.k))
         return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
-    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
+    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, part, part_bytes);
 }
 
 static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
@@ -219,7 +231,7 @@ nhm_status nhm_fp8_dequant_channel_bf16(const uint8_t* w, const float* w_scale, 
 
 size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type) {
     if (m <= 0 || n <= 0 || k <= 0) return 0;
-    return linear_ws(m, k, a_type);
+    return linear_ws(m, n, k, a_type);
 }
 
 nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
@@ -249,7 +261,7 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
         return fail(NHM_ERR_ALIGN, "a must be 16-byte aligned with 16-byte row stride");
     if (!aligned(out, out_type == NHM_F32 ? 4 : 2))
         return fail(NHM_ERR_ALIGN, "out must be aligned to its element size");
-    const size_t need = linear_ws(m, w->k, a_type);
+    const size_t need = linear_codes_ws(m, w->k, a_type);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (ws && !aligned(ws, 256)) return fail(NHM_ERR_ALIGN, "ws must be 256-byte aligned");
@@ -264,8 +276,12 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
         aq = q;
         lda = w->k;
     }
-    if (out_type == NHM_F32) return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out));
-    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, st);
+    // the split-k partials after the codes, where the workspace holds them
+    const size_t pb = gemm_part_bytes(m, w->n, w->k);
+    float* part = pb > 0 && ws && ws_bytes >= need + pb ? reinterpret_cast<float*>(wsb + need) : nullptr;
+    if (out_type == NHM_F32)
+        return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out), part, part ? pb : 0);
+    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, st, nullptr, part, part ? pb : 0);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
@@ -421,7 +437,9 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     if (n_tokens > 0) {
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
-        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, st)) != NHM_OK) return s;
+        if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, st, nullptr,
+                         reinterpret_cast<float*>(wsb + w.part), w.part_bytes)) != NHM_OK)
+            return s;
     }
     PrefillArgs a;
     // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every later
@@ -475,7 +493,8 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     a.q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
     if ((s = launch_prefill_mid(a, st)) != NHM_OK) return s;
     if (n_tokens > 0)
-        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, st);
+        return project(a.q_out, l.d_inner, n_tokens, p->out_proj, out, H, st, nullptr,
+                       reinterpret_cast<float*>(wsb + w.part), w.part_bytes);
     return NHM_OK;
 }
 

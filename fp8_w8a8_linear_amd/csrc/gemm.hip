@@ -40,6 +40,11 @@ struct GemmArgs {
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
     uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
     float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
+    // split k (ring tile kernel): blocks [s * tiles, (s + 1) * tiles) sum the s-th of ksplit
+    // contiguous k ranges into part [ksplit, m, n] (raw f32 sums), which splitk_reduce_kernel
+    // adds up in split order, scales and rounds
+    int ksplit = 1;
+    float* part = nullptr;
 };
 
 // Row r of a 128-byte-wide LDS tile holds its 16-byte chunk c at slot c ^ (r & 7):
@@ -424,7 +429,8 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     // activation and 4 weight panels through its L2.
     const int ntn = (int)((g.n + TN - 1) / TN), ntm = (int)((g.m + TM - 1) / TM);
     const int total = ntn * ntm;
-    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int bid = (int)(blockIdx.x % (unsigned)total), ks = (int)(blockIdx.x / (unsigned)total);
+    const int x = bid & 7, loc = bid >> 3;
     const int j = x * (total >> 3) + min(x, total & 7) + loc;
     constexpr int kGroupM = 8;
     const int grp = j / (kGroupM * ntn), within = j - grp * kGroupM * ntn;
@@ -464,8 +470,14 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
             dbase[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
         }
     }
-    auto issue = [&](int s) {   // stage s (s may run past k: its loads are out of range, zeros)
-        const uint32_t k0 = (uint32_t)s * kWK;
+    // this block's k stages: s_beg .. s_beg + nk - 1 (all of k without a split)
+    const int nk_all = (int)((g.k + kWK - 1) / kWK);
+    const int kper = (nk_all + g.ksplit - 1) / g.ksplit;
+    const int s_beg = ks * kper;
+    const int nk = min(kper, nk_all - s_beg);   // >= 1: the launcher leaves no split empty
+    auto issue = [&](int s) {   // stage s (past k its loads are out of range, zeros; past this
+                                // split's range they are loaded and never read)
+        const uint32_t k0 = (uint32_t)(s_beg + s) * kWK;
         const bool kin = (int64_t)k0 + kc < g.k;
         uint8_t* sb = smem + (s % kRing) * kStage;
 #pragma unroll
@@ -494,7 +506,6 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
 
-    const int nk = (int)((g.k + kWK - 1) / kWK);
     // Step kt: wait for stage kt + 1 (this thread's loads), barrier (all of them landed, and
     // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
     // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
@@ -530,6 +541,24 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     // 16-byte chunk cn of row ml at slot cn ^ (ml & 15) with its two 8-byte halves swapped when
     // bit 3 xor bit 4 of ml is set: the 8-byte writes of 32 rows at one n land in 32 distinct
     // slots of the 256-byte bank window. Each half-wave then stores one whole 512-byte row.
+    if (g.part) {
+        // split k: this split's raw sums, f32 [m, n] slice ks of the partial buffer
+        float* pt = g.part + (int64_t)ks * g.m * g.n;
+        const float one[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int i = 0; i < kNI; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int64_t nb = n0 + wn * (TN / 2) + i * 32 + gq * 8 + q * 4;
+#pragma unroll
+                for (int jx = 0; jx < kJX; ++jx) {
+                    const int64_t mm = m0 + wm * (TM / 4) + jx * 32 + r32;
+                    const v4f a4 = {acc[i][jx][4 * gq], acc[i][jx][4 * gq + 1], acc[i][jx][4 * gq + 2], acc[i][jx][4 * gq + 3]};
+                    store_tile_f32(pt, g.n, mm, nb, g.m, g.n, a4, one, (g.n & 3) == 0 && mm < g.m && nb + 3 < g.n);
+                }
+            }
+        return;
+    }
     const float sa = *g.a_scale;
     if (g.out_f32) {
         // f32 output: each lane stores its four consecutive n of one m row straight from the
@@ -596,6 +625,52 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     }
 }
 
+// Split-k epilogue: out[m, n] = (sum over s of part[s, m, n], in split order) * a_scale *
+// w_scale[n], rounded once (bf16) or stored as f32. Four consecutive outputs per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t mn = g.m * g.n;
+    if (e0 >= mn) return;
+    const float sa = *g.a_scale;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if ((g.n & 3) == 0) {   // the four share a row; 16-byte partial loads
+        for (int s = 0; s < g.ksplit; ++s) {
+            const float4 p = *reinterpret_cast<const float4*>(g.part + (int64_t)s * mn + e0);
+            v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+        }
+        const int64_t mm = e0 / g.n, nn = e0 - mm * g.n;
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = v[r] * (sa * g.w_scale[nn + r]);
+        if (g.out_f32) {
+            float* d = g.out_f32 + mm * g.ld_out + nn;
+            if (g.vec_out) {
+                *reinterpret_cast<float4*>(d) = make_float4(o[0], o[1], o[2], o[3]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[r] = o[r];
+            }
+        } else {
+            uint16_t* d = g.out + mm * g.ld_out + nn;
+            if (g.vec_out) {
+                *reinterpret_cast<uint2*>(d) = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[r] = (uint16_t)f32_to_bf16(o[r]);
+            }
+        }
+        return;
+    }
+    for (int r = 0; r < 4 && e0 + r < mn; ++r) {
+        const int64_t e = e0 + r, mm = e / g.n, nn = e - mm * g.n;
+        float acc = 0.f;
+        for (int s = 0; s < g.ksplit; ++s) acc += g.part[(int64_t)s * mn + e];
+        const float o = acc * (sa * g.w_scale[nn]);
+        if (g.out_f32) g.out_f32[mm * g.ld_out + nn] = o;
+        else g.out[mm * g.ld_out + nn] = (uint16_t)f32_to_bf16(o);
+    }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <int BM, int WN>
@@ -613,9 +688,44 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 // 160 of its tiles (m = 1024 for in_proj, m = 4096 for out_proj: 45 vs 54 us and
 // 60 vs 74 us; at m = 15,360 477 vs 652 us and 187 vs 253 us) and trails below
 // (123 tiles at m = 641: 43 vs 36 us).
+// Split k for m <= 640 where the ring tiles are too few to fill the chip (the panel kernel's
+// case): the 192 x 128 ring tile over S k ranges puts fewer operand bytes on the busiest CU
+// than a 64 x 128 panel over all of k, at the price of the f32 partials and the reduction.
+// Costs in bytes of one CU's operand delivery (~37 GB/s); the partials' cost is fitted to
+// three measured shapes (split against panel: 512 x 2688 x 4096 25.3 vs 20.9 us, 64 x 4096 x
+// 4096 16.2 vs 19.3 us, 200 x 10304 x 2688 25.9 vs 26.4 us): ~6 us fixed (230 KB) plus
+// ~0.35 us per MB of partials (bytes / 77) -- the tiles write them in one burst at their end.
+// The estimate still missed 128 x 2688 x 4096 (split 20.7 vs panel 19.7 us, 42 panel
+// workgroups), so a split is taken only where the panel kernel would run at most 32 workgroups
+// (7/8 of the chip idle). Returns the S that minimises the estimate there, else 1.
+static int split_k(int64_t m, int64_t n, int64_t k) {
+    if (m > 640 || m <= 0 || n <= 0 || k <= 0) return 1;
+    const int64_t half_tiles = ((n + kWT - 1) / kWT) * ((m + 127) / 128);
+    const int64_t t192 = ((n + 191) / 192) * ((m + 127) / 128);
+    if (half_tiles >= 160 || t192 >= 160) return 1;
+    const int64_t nk = (k + kWK - 1) / kWK;
+    const int64_t panel_wgs = 8 * ((m + 63) / 64) * (((n + 127) / 128 + 7) / 8);
+    if (panel_wgs > 32) return 1;
+    int64_t best = (panel_wgs + 255) / 256 * (64 + 128) * k;
+    int split = 1;
+    for (int S = 2; S <= 8; ++S) {
+        const int64_t kper = (nk + S - 1) / S;
+        if (kper * (S - 1) >= nk) continue;   // a split would be empty
+        const int64_t cost = (t192 * S + 255) / 256 * ((192 + 128) * kper * kWK + 4 * 192 * 128) +
+                             S * m * n * 4 / 77 + 230000;
+        if (cost < best) { best = cost; split = S; }
+    }
+    return split;
+}
+
+size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k) {
+    const int S = split_k(m, n, k);
+    return S > 1 ? (size_t)S * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st, float* out_f32) {
+                       hipStream_t st, float* out_f32, float* part, size_t part_bytes) {
     GemmArgs g{a, lda, m, w, w_scale, a_scale, n, k, out, ld_out,
                out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
                        : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0,
@@ -638,6 +748,16 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         return check_launch("gemm (256 x 128)");
     }
     if (m <= 640 && offsets_fit) {   // too few ring tiles to fill the chip
+        const int S = split_k(m, n, k);
+        if (S > 1 && part && part_bytes >= gemm_part_bytes(m, n, k) && (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
+            g.ksplit = S;
+            g.part = part;
+            tile256_kernel<192, 128><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
+            nhm_status s = check_launch("gemm (192 x 128, split k)");
+            if (s != NHM_OK) return s;
+            splitk_reduce_kernel<<<dim3((unsigned)((m * n + 1023) / 1024)), dim3(256), 0, st>>>(g);
+            return check_launch("gemm split-k reduce");
+        }
         launch_panel<64, 32>(g, st);
         return check_launch("gemm (panel)");
     }

@@ -35,9 +35,13 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
                        float* out_f32 = nullptr);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
+// part (16-byte aligned, part_bytes >= gemm_part_bytes(m, n, k)): scratch for the split-k
+// partials of the shapes that take a split (m <= 640 with too few ring tiles); without it
+// those shapes run unsplit.
+size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st, float* out_f32 = nullptr);
+                       hipStream_t st, float* out_f32 = nullptr, float* part = nullptr, size_t part_bytes = 0);
 
 // ---- decode SSM state update (decode.hip)
 // The kernel also runs the causal conv + SiLU of the channels it reads (the head's x, the

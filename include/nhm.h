@@ -162,7 +162,9 @@ NHM_API nhm_status nhm_fp8_quantize_static(const uint16_t* x, int64_t rows, int6
 NHM_API nhm_status nhm_fp8_dequant_channel_bf16(const uint8_t* w, const float* w_scale, int64_t n, int64_t k,
                                         int64_t ld_w, uint16_t* out, int64_t ld_out, void* stream);
 
-/* Workspace bytes nhm_fp8_linear needs for this shape and input type. */
+/* Workspace bytes for nhm_fp8_linear on this shape and input type: the activation codes
+ * of a bf16 input (required), then, for the narrow shapes that split k (see below), room
+ * for the f32 partials (optional: a workspace without it runs those shapes unsplit). */
 NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, nhm_dtype a_type);
 
 /* out[i, j] = bf16( (sum_k val(a_q[i, k]) * val(w[j, k])) * a_scale * w_scale[j] ),
@@ -175,14 +177,19 @@ NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, n
  *   w      (host struct of device pointers)
  *   out    (device) bf16 [m, ld_out], ld_out >= n; must not overlap a (rows that
  *          are 8-byte aligned are stored 4 features at a time)
- *   ws     (device) >= nhm_fp8_linear_workspace_bytes(m, n, k, a_type) bytes (0 for an
- *          e4m3 input, where ws may be NULL)
+ *   ws     (device, 256-byte aligned) nhm_fp8_linear_workspace_bytes(m, n, k, a_type)
+ *          bytes; the bf16 input's codes (m * k bytes, rounded up to 256) are required,
+ *          the rest only enables the split-k path; with an e4m3 input ws may be NULL
  * m == 0 is a valid no-op. m <= 16 (k <= 16384, weight under 2 GiB) runs the
  * weight-streaming GEMV, which sums the products exactly in f32 (the codes are
  * converted to bf16, exact for every e4m3 value, and summed by the bf16 MFMA).
  * Larger m runs the tiled e4m3 MFMA GEMM, whose 128-product reductions are coarser
  * than f32: measured on MI355X, within ~2^-17 of sum |a w| per 128 products (the
  * result still lies within 2^-8 |out| + 2^-16 sum |a w| of the exact one).
+ * Where 16 < m <= 640 leaves the 64 x 128 tiles on at most 32 workgroups (narrow n, long
+ * k) and the workspace holds the partials, k is split over 2-8 workgroups per tile and
+ * their f32 partial sums are added in split order by a second kernel, then scaled and
+ * rounded once.
  * Results are deterministic (no atomics).
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
 NHM_API nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
@@ -261,7 +268,8 @@ NHM_API nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* h
                             void* stream);
 
 /* Workspace layout of nhm_mixer_prefill for up to n_tokens tokens in up to n_seqs
- * sequences with SSD chunk length `chunk`.
+ * sequences with SSD chunk length `chunk`. total also covers scratch the layout does not
+ * name: the chunk plan, per-chunk decays and states, and the projections' split-k partials.
  * Errors: NHM_ERR_NULL, NHM_ERR_UNSUPPORTED, NHM_ERR_SHAPE. */
 NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_tokens, int32_t n_seqs,
                                        int32_t chunk, nhm_ws_layout* out);

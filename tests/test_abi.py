@@ -186,3 +186,14 @@ def test_workspace_sizes_grow(nhm):
     assert a["q_in"] < a["zxbcdt"] < a["xbc_conv"] < a["y"] < a["norm"] < a["q_out"] < a["total"]
     d = nhm.decode_ws_layout(8)
     assert d["q_out"] + 8 * 4096 <= d["total"]
+
+
+def test_linear_workspace_split_partials(nhm):
+    """The workspace query: a narrow shape that splits k reports room for its f32 partials
+    (at least two splits of m x n), after the bf16 input's codes; other shapes report none."""
+    need = nhm.fp8_linear_workspace_bytes(64, 4096, 4096, nhm.NHM_E4M3)
+    assert need >= 2 * 64 * 4096 * 4 and need % 256 == 0
+    assert nhm.fp8_linear_workspace_bytes(64, 4096, 4096, nhm.NHM_BF16) == 64 * 4096 + need
+    for m, n, k in [(512, 10304, 2688), (512, 2688, 4096), (8, 10304, 2688), (4096, 2688, 4096)]:
+        assert nhm.fp8_linear_workspace_bytes(m, n, k, nhm.NHM_E4M3) == 0
+        assert nhm.fp8_linear_workspace_bytes(m, n, k, nhm.NHM_BF16) == (m * k + 255) // 256 * 256

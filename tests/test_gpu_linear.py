@@ -101,6 +101,44 @@ def test_linear_per_tensor_weight_scale(nhm, m, n, k):
     _check(nhm, a, w, ws, sa)
 
 
+# Narrow shapes whose panel launch would leave most of the chip idle: with the workspace the
+# query reports, the 192 x 128 ring tile over S k ranges plus the reduction (33 x 1002: ragged
+# m and n, n % 4 != 0 takes the reduction's element path); an e4m3 input with no workspace
+# runs the unsplit 64 x 128 panel kernel. Both meet the bound, with bf16 and with f32 output.
+@pytest.mark.parametrize("m,n,k", [(64, 4096, 4096), (48, 2688, 4096), (17, 4096, 4096), (33, 1002, 4096)])
+@pytest.mark.parametrize("out_type", ["bf16", "f32"])
+def test_linear_split_k_and_unsplit(nhm, m, n, k, out_type):
+    import ctypes as C
+    from oracle import bf16_to_f64, e4m3_decode, fp8_linear, quantize_static
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=11)
+    q = quantize_static(a, sa)
+    ref = fp8_linear(q, w, ws, sa)
+    S = np.abs(e4m3_decode(q)) @ np.abs(e4m3_decode(w)).T * np.float64(sa[0]) * ws.astype(np.float64)[None, :]
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    need = nhm.fp8_linear_workspace_bytes(m, n, k, nhm.NHM_E4M3)
+    assert need >= 2 * m * n * 4                         # room for the partials of at least two splits
+    qd = dev(q)
+    f32 = out_type == "f32"
+    outs = []
+    for wsb in (torch.zeros(need, dtype=torch.uint8, device="cuda"), None):
+        out = torch.empty((m, n), dtype=torch.float32 if f32 else torch.int16, device="cuda")
+        st = nhm.lib.nhm_fp8_linear_ex(C.c_void_p(qd.data_ptr()), nhm.NHM_E4M3, m, k, C.byref(W.struct),
+                                       C.c_void_p(out.data_ptr()), nhm.NHM_F32 if f32 else nhm.NHM_BF16, n,
+                                       None if wsb is None else C.c_void_p(wsb.data_ptr()),
+                                       0 if wsb is None else wsb.numel(),
+                                       C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, nhm.lib.nhm_last_error()
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().astype(np.float64) if f32 else bf16_to_f64(host(out)))
+    for got in outs:
+        err = np.abs(got - ref)
+        bound = (2.0 ** -22 if f32 else 2.0 ** -8) * np.abs(ref) + 2.0 ** -16 * S
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert np.all(err <= bound), f"at {worst}: got {got[worst]} ref {ref[worst]} bound {bound[worst]}"
+
+
 # ld_pad 13 makes the row stride odd: the kernels fall back from 8-byte stores
 @pytest.mark.parametrize("m", [2, 100, 700])
 @pytest.mark.parametrize("ld_pad", [12, 13])
