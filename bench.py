@@ -8,10 +8,10 @@ headline line), the same step on bf16 state pools (decode_bf16_state), prefill o
 
 A step is one decode token for each of 8 sequences through all 23 mixer blocks
 (nhm_mixer_decode per block, state rows updated in place), replayed as one HIP
-graph. Inputs are seeded synthetic tensors already resident in HBM. Before timing,
-layers 0 and 1 of one step are checked against the oracle (block parity and the
-updated f32 states); that same oracle run, timed on the host cores, is the
-cpu_baseline. Prints ONE JSON line on stdout; progress goes to stderr.
+graph. Inputs are seeded synthetic tensors already resident in HBM. After all GPU
+timing, layers 0 and 1 of one step from their seeded pools are checked against the
+oracle (block parity and the updated f32 states); that same oracle run, timed on the
+host cores, is the cpu_baseline. Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
@@ -139,42 +139,6 @@ def main():
     def step(stream=None):
         for l in range(N_LAYERS):
             nhm.mixer_decode(params[l], acts[l], sl, spools[l], cpools[l], acts[l + 1], ws, stream=stream)
-
-    # ------------------------------------------------------------ parity sample + cpu baseline
-    parity, cpu = None, None
-    if not args.no_cpu:
-        from oracle import mixer_decode as oracle_decode
-        from oracle.parity import block_parity, rel_l2
-        import threadpoolctl
-        parity = {}
-        t_layers = []
-        x_in = x_host
-        for layer in range(2):
-            nhm.mixer_decode(params[layer], acts[layer], sl, spools[layer], cpools[layer], acts[layer + 1], ws)
-            torch.cuda.synchronize()
-            out = acts[layer + 1].cpu().numpy().view(np.uint16)
-            wsn = ws.cpu().numpy()
-            q = wsn[lay["q_out"]:lay["q_out"] + BATCH * INNER].reshape(BATCH, INNER)
-            nrm = wsn[lay["norm"]:lay["norm"] + BATCH * INNER * 2].view(np.uint16).reshape(BATCH, INNER)
-            st_gpu = spools[layer].cpu().numpy()
-            sp, cp = host_pools[layer]
-            spr, cpr = sp.copy(), cp.copy()
-            tc = time.perf_counter()
-            ref, res = oracle_decode(host_params[layer], x_in, sl_host, spr, cpr)
-            t_layers.append(time.perf_counter() - tc)
-            st_err = max(rel_l2(st_gpu[s], spr[s]) for s in sl_host)
-            assert st_err <= 1e-3, f"layer {layer}: state rel l2 {st_err}"
-            entry = {"state_rel_l2_max": float(f"{st_err:.3e}")}
-            entry.update(block_parity(out, q, nrm, ref, res["norm"], res["q_out"], host_params[layer]))
-            parity[f"layer{layer}"] = entry
-            x_in = out
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] + [1])
-        t_layer = float(np.mean(t_layers))
-        cpu = {"value": round(BATCH / (N_LAYERS * t_layer), 4), "unit": "tokens/s", "cores": int(cores),
-               "kind": "oracle",
-               "sample": f"oracle decode of layers 0-1 of one B={BATCH} step ({t_layer:.2f} s/layer), scaled to 23 layers"}
-        log(f"parity sample ok: {parity}; oracle {t_layer:.2f} s/layer on {cores} threads")
 
     # ------------------------------------------------------------ graph capture and timing
     cap = torch.cuda.Stream()
@@ -384,6 +348,49 @@ def main():
     gemm_us = gemm["in_proj"]["us"] + gemm["out_proj"]["us"]
     gemm_tflops = 2 * T * 38707200 / (gemm_us * 1e-6) / 1e12
     log(f"prefill 512: {pre_us:.1f} us/block, {T / (pre_us * 1e-6):.0f} tokens/s; GEMMs {gemm}")
+
+    # ------------------------------------------------------------ parity sample + cpu baseline
+    # after every GPU measurement (the oracle's host threads cannot disturb them); layers 0-1
+    # get their initial pools back, so the sample checks one step from the seeded state
+    parity, cpu = None, None
+    if not args.no_cpu:
+        for layer in range(2):
+            sp, cp = host_pools[layer]
+            spools[layer].copy_(up(sp))
+            cpools[layer].copy_(up(cp))
+        torch.cuda.synchronize()
+        from oracle import mixer_decode as oracle_decode
+        from oracle.parity import block_parity, rel_l2
+        import threadpoolctl
+        parity = {}
+        t_layers = []
+        x_in = x_host
+        for layer in range(2):
+            nhm.mixer_decode(params[layer], acts[layer], sl, spools[layer], cpools[layer], acts[layer + 1], ws)
+            torch.cuda.synchronize()
+            out = acts[layer + 1].cpu().numpy().view(np.uint16)
+            wsn = ws.cpu().numpy()
+            q = wsn[lay["q_out"]:lay["q_out"] + BATCH * INNER].reshape(BATCH, INNER)
+            nrm = wsn[lay["norm"]:lay["norm"] + BATCH * INNER * 2].view(np.uint16).reshape(BATCH, INNER)
+            st_gpu = spools[layer].cpu().numpy()
+            sp, cp = host_pools[layer]
+            spr, cpr = sp.copy(), cp.copy()
+            tc = time.perf_counter()
+            ref, res = oracle_decode(host_params[layer], x_in, sl_host, spr, cpr)
+            t_layers.append(time.perf_counter() - tc)
+            st_err = max(rel_l2(st_gpu[s], spr[s]) for s in sl_host)
+            assert st_err <= 1e-3, f"layer {layer}: state rel l2 {st_err}"
+            entry = {"state_rel_l2_max": float(f"{st_err:.3e}")}
+            entry.update(block_parity(out, q, nrm, ref, res["norm"], res["q_out"], host_params[layer]))
+            parity[f"layer{layer}"] = entry
+            x_in = out
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        t_layer = float(np.mean(t_layers))
+        cpu = {"value": round(BATCH / (N_LAYERS * t_layer), 4), "unit": "tokens/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"oracle decode of layers 0-1 of one B={BATCH} step ({t_layer:.2f} s/layer), scaled to 23 layers"}
+        log(f"parity sample ok: {parity}; oracle {t_layer:.2f} s/layer on {cores} threads")
 
     line = {
         "metric": "Mamba2-mixer tokens/s (decode b=8, prefill 512) + % HBM / fp8-MFMA peak",
