@@ -80,13 +80,20 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
 // ---------------------------------------------------------------- workspace layouts
 
 // bytes of the e4m3 copy of a bf16 activation (the only workspace nhm_fp8_linear needs)
+// The weight-streaming GEMV serves m <= 16 (k up to 16384, weights under 2 GiB: its buffer
+// descriptors take 32-bit offsets); the tiled GEMM the rest.
+static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
+
+// Split-k partials of one projection: none where the GEMV runs.
+static size_t proj_part_bytes(int64_t m, int64_t n, int64_t k) { return use_gemv(m, n, k) ? 0 : gemm_part_bytes(m, n, k); }
+
 // The linear's workspace: the activation codes of a bf16 input (required), then the split-k
 // partials of the shapes that take a split (optional: without them those shapes run unsplit).
 static size_t linear_codes_ws(int64_t m, int64_t k, nhm_dtype t) {
     return t == NHM_BF16 ? align_up((size_t)m * (size_t)k, 256) : 0;
 }
 static size_t linear_ws(int64_t m, int64_t n, int64_t k, nhm_dtype t) {
-    return linear_codes_ws(m, k, t) + align_up(gemm_part_bytes(m, n, k), 256);
+    return linear_codes_ws(m, k, t) + align_up(proj_part_bytes(m, n, k), 256);
 }
 
 struct MixerWs {
@@ -109,6 +116,8 @@ static MixerWs decode_ws(const nhm_geometry* g, int32_t batch) {
     w.pub.y = take(B * l.d_inner * 2);
     w.pub.norm = take(B * l.d_inner * 2);
     w.pub.q_out = take(B * l.d_inner);
+    w.part_bytes = batch > 32 ? proj_part_bytes(batch, g->hidden, l.d_inner) : 0;   // out_proj above 32 rows
+    w.part = take(w.part_bytes);
     w.pub.total = off;
     return w;
 }
@@ -133,15 +142,12 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
     w.pub.y = take(Ts * l.d_inner * 2);
     w.pub.norm = take(Ts * l.d_inner * 2);
     w.pub.q_out = take(Ts * l.d_inner);
-    w.part_bytes = std::max(gemm_part_bytes(T, l.d_in_proj, g->hidden), gemm_part_bytes(T, g->hidden, l.d_inner));
+    w.part_bytes = std::max(proj_part_bytes(T, l.d_in_proj, g->hidden), proj_part_bytes(T, g->hidden, l.d_inner));
     w.part = take(w.part_bytes);
     w.pub.total = off;
     return w;
 }
 
-// The weight-streaming GEMV serves m <= 16 (k up to 16384, weights under 2 GiB: its buffer
-// descriptors take 32-bit offsets); the tiled GEMM the rest.
-static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
 
 // One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
 // part / part_bytes: scratch for the GEMM's split-k partials (nullptr: no split).
@@ -277,7 +283,7 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
         lda = w->k;
     }
     // the split-k partials after the codes, where the workspace holds them
-    const size_t pb = gemm_part_bytes(m, w->n, w->k);
+    const size_t pb = proj_part_bytes(m, w->n, w->k);
     float* part = pb > 0 && ws && ws_bytes >= need + pb ? reinterpret_cast<float*>(wsb + need) : nullptr;
     if (out_type == NHM_F32)
         return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out), part, part ? pb : 0);
@@ -382,6 +388,14 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     ga.c_off = l.c_off;
     ga.d_state = p->g.d_state;
     if ((s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
+    // out_proj above 32 rows in one GEMM call (which splits k for these narrow shapes), reading
+    // the weight once instead of once per 16 rows: one block at B = 64 104.9 -> 98.0 us; at
+    // B = 32 two GEMV launches stay ahead (60.0 against 61.6 us). in_proj stays on the GEMV per
+    // 16 rows: its exact f32 sums feed dt, which every later decay exponentiates (the GEMM's
+    // coarser sums would need the dt recompute the prefill runs).
+    if (batch > 32)
+        return project(q_out, l.d_inner, batch, p->out_proj, out, H, st, nullptr,
+                       reinterpret_cast<float*>(wsb + w.part), w.part_bytes);
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
         s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, st);
