@@ -17,15 +17,17 @@
 //    one XCD so the panel is fetched into that XCD's L2 once. Loads go through
 //    buffer descriptors, whose range check returns zeros past the operand's end,
 //    so ragged edges and padded steps need no branches in the loop.
-//  * ring tile kernel, 256 x 256, 256 x 128 or 192 x 128 (enough tiles to fill the chip):
-//    both operand tiles stream into an LDS ring of 64-byte k-slices (5 to 8 stages, as many
-//    as fit 160 KB) by direct-to-LDS buffer loads (no register round trip; the range check
+//  * ring tile kernels, 256 x 256 or 256 x 128 with 64-byte k-slices and 192 x 128 with
+//    128-byte ones (enough tiles to fill the chip): both operand tiles stream into an LDS ring
+//    of k-slices (4 to 6 stages, as many as fit 160 KB) by direct-to-LDS buffer loads (no register round trip; the range check
 //    zero-fills ragged rows and k), eight waves on the 32x32x64 MFMA read the operands of
 //    the next stage while the MFMAs of the current one run, and the bf16 result leaves
 //    through LDS so that every store writes whole output rows. Each CU receives operands
 //    at a rate bounded by the requests it keeps in flight, so the operand bytes a CU must
 //    pull set the time: wide tiles (fewer bytes per MAC) at large m, and at m <= 640 the
-//    tile shape whose busiest CU pulls the fewest bytes.
+//    tile shape whose busiest CU pulls the fewest bytes; and whole 128-byte line requests
+//    carry twice the bytes of 64-byte ones per request in flight, where the LDS has room for
+//    128-byte slices.
 //  * 128 x 128 tile kernel (remaining shapes): both operands staged through
 //    double-buffered LDS, four waves of 64 x 64.
 #include <stdint.h>
@@ -350,9 +352,9 @@ constexpr int kWT = 256;               // workgroup tile extent in n (and in m f
 constexpr int kWK = 64;                // k bytes per ring stage (one 32x32x64 MFMA deep)
 constexpr int kWStage = kWT * kWK;     // the weight tile's part of a stage, 16 KB
 
-// Ring geometry of a TN (n) x TM (m) tile: a stage holds TN weight rows then TM activation
-// rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for 256 x 256, 6 x 24 KB
-// for 256 x 128, 8 x 20 KB for 192 x 128). The eight waves are 2 (n) x 4 (m), each TN / 2 x
+// Ring geometry of a TN (n) x TM (m) tile with 64-byte k-slices: a stage holds TN weight rows
+// then TM activation rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for
+// 256 x 256, 6 x 24 KB for 256 x 128). The eight waves are 2 (n) x 4 (m), each TN / 2 x
 // TM / 4. A stage is (TN + TM) / 16 DMA blocks of 16 rows (1 KB each, block b at b KB of the
 // stage); each wave issues kLoads of them per stage.
 template <int TN, int TM>
@@ -408,134 +410,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Operands under 2^31 bytes (buffer offsets). Grid = number of TN x TM tiles, 512 threads.
+// Block -> (tile origin m0, n0; k split ks) of a ring kernel. Blocks go to the 8 XCDs round
+// robin; each XCD takes a contiguous share of the tiles in an order that walks 8 m-tiles per
+// n-tile, so the ~32 tiles an XCD holds at once share 8 activation and 4 weight panels
+// through its L2. With a k split, blocks [s * tiles, (s + 1) * tiles) take split s.
 template <int TN, int TM>
-__global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
-    using RS = RingShape<TN, TM>;
-    constexpr int kStage = RS::kStage, kRing = RS::kRing, kNI = RS::kNI, kJX = RS::kJX, kLoads = RS::kLoads;
-    constexpr int kWStageT = TN * kWK;              // the weight rows' part of a stage
-    static_assert((TN == 256 && (TM == 256 || TM == 128)) || (TN == 192 && TM == 128), "tile shape");
-    static_assert(kRing >= 4 && (kRing - 2) * kLoads < 64, "ring depth and the vmcnt field");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
-    // the epilogue stages the bf16 tile in the ring as TM rows of 512 bytes (TN <= 256)
-    static_assert(kRing * kStage >= TM * 512, "the epilogue stages the whole bf16 tile in the ring");
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n TN / 2 x m TM / 4
-    const int r32 = lane & 31, q = lane >> 5;
-
-    // Blocks go to the 8 XCDs round robin; each XCD takes a contiguous share of the tiles in an
-    // order that walks 8 m-tiles per n-tile, so the ~32 tiles an XCD holds at once share 8
-    // activation and 4 weight panels through its L2.
+__device__ __forceinline__ void ring_tile(const GemmArgs& g, int64_t& m0, int64_t& n0, int& ks) {
     const int ntn = (int)((g.n + TN - 1) / TN), ntm = (int)((g.m + TM - 1) / TM);
     const int total = ntn * ntm;
-    const int bid = (int)(blockIdx.x % (unsigned)total), ks = (int)(blockIdx.x / (unsigned)total);
+    const int bid = (int)(blockIdx.x % (unsigned)total);
+    ks = (int)(blockIdx.x / (unsigned)total);
     const int x = bid & 7, loc = bid >> 3;
     const int j = x * (total >> 3) + min(x, total & 7) + loc;
     constexpr int kGroupM = 8;
     const int grp = j / (kGroupM * ntn), within = j - grp * kGroupM * ntn;
     const int gms = min(kGroupM, ntm - grp * kGroupM);
-    const int64_t m0 = (int64_t)(grp * kGroupM + within % gms) * TM, n0 = (int64_t)(within / gms) * TN;
+    m0 = (int64_t)(grp * kGroupM + within % gms) * TM;
+    n0 = (int64_t)(within / gms) * TN;
+}
 
-    // DMA. TN = 256: wave w fills weight rows 32 w .. 32 w + 31 and activation rows (TM / 8) w
-    // .. (TM / 8) (w + 1) - 1 of a stage. TN = 192: wave w takes the 16-row blocks w, w + 8,
-    // w + 16 of the stage's 20 (weight blocks first); where w + 16 is past the last block it
-    // loads block w + 8 a second time (the same bytes to the same place), so that every wave
-    // issues kLoads instructions per stage and the waits count alike. 16 rows per instruction;
-    // lane l lands in slot l of the instruction's 1 KB: row 16 i + l / 4, chunk slot l % 4,
-    // which holds the logical chunk kc / 16 under the swizzle (the swizzle depends on the row
-    // modulo 16 only).
-    const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
-    const int lr = lane >> 2;
-    const int kc = ((lane & 3) ^ (((lr >> 1) ^ (lr >> 2)) & 3)) * 16;
-    uint32_t dbase[kLoads];    // this lane's source offset of each of the wave's blocks (k = 0)
-    int dlds[kLoads];          // the block's byte offset in a stage
-    bool dw[kLoads];           // weight block (else activation)
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        int blk;
-        if constexpr (TN == 256) {
-            blk = i < 2 ? wave * 2 + i : RS::kBlocks - TM / 16 + wave * kJX + (i - 2);
-        } else {
-            blk = wave + 8 * i;
-            if (blk >= RS::kBlocks) blk -= 8;
-        }
-        dw[i] = blk < TN / 16;
-        dlds[i] = blk * 1024;
-        if (dw[i]) {
-            const int row = blk * 16 + lr;
-            dbase[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
-        } else {
-            const int row = (blk - TN / 16) * 16 + lr;
-            dbase[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
-        }
-    }
-    // this block's k stages: s_beg .. s_beg + nk - 1 (all of k without a split)
-    const int nk_all = (int)((g.k + kWK - 1) / kWK);
-    const int kper = (nk_all + g.ksplit - 1) / g.ksplit;
-    const int s_beg = ks * kper;
-    const int nk = min(kper, nk_all - s_beg);   // >= 1: the launcher leaves no split empty
-    auto issue = [&](int s) {   // stage s (past k its loads are out of range, zeros; past this
-                                // split's range they are loaded and never read)
-        const uint32_t k0 = (uint32_t)(s_beg + s) * kWK;
-        const bool kin = (int64_t)k0 + kc < g.k;
-        uint8_t* sb = smem + (s % kRing) * kStage;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) dma16(dw[i] ? wrs : ars, sb + dlds[i], kin ? dbase[i] + k0 : kOutOfRange);
-    };
-    auto read_ops = [&](int s, v8i (&wop)[kNI], v8i (&aop)[kJX]) {
-        const uint8_t* sw = smem + (s % kRing) * kStage;
-        const uint8_t* sa = sw + kWStageT;
-#pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-            const int row = wn * (TN / 2) + i * 32 + r32;
-            wop[i] = cat8(lds16(sw + swz64(row, 2 * q)), lds16(sw + swz64(row, 2 * q + 1)));
-        }
-#pragma unroll
-        for (int jx = 0; jx < kJX; ++jx) {
-            const int row = wm * (TM / 4) + jx * 32 + r32;
-            aop[jx] = cat8(lds16(sa + swz64(row, 2 * q)), lds16(sa + swz64(row, 2 * q + 1)));
-        }
-    };
-
-    v16f acc[kNI][kJX];
-#pragma unroll
-    for (int i = 0; i < kNI; ++i)
-#pragma unroll
-        for (int jx = 0; jx < kJX; ++jx)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
-
-    // Step kt: wait for stage kt + 1 (this thread's loads), barrier (all of them landed, and
-    // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
-    // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
-    // stage kt (read one step earlier) run.
-    auto step = [&](int kt, const v8i (&cw)[kNI], const v8i (&ca)[kJX], v8i (&nw)[kNI], v8i (&na)[kJX]) {
-        wait_vmcnt<(kRing - 3) * kLoads>();
-        __syncthreads();
-        issue(kt + kRing - 1);
-        if (kt + 1 < nk) read_ops(kt + 1, nw, na);
-        __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs
-#pragma unroll
-        for (int i = 0; i < kNI; ++i)
-#pragma unroll
-            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
-        __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
-    };
-#pragma unroll
-    for (int s = 0; s < kRing - 1; ++s) issue(s);
-    v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
-    wait_vmcnt<(kRing - 2) * kLoads>();
-    __syncthreads();
-    read_ops(0, w0, a0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        step(kt, w0, a0, w1, a1);
-        step(kt + 1, w1, a1, w0, a0);
-    }
-    if (kt < nk) step(kt, w0, a0, w1, a1);
-    wait_vmcnt<0>();   // the ring's trailing loads (past k) before the ring is reused
-
+// The end of a ring kernel (all of its loads retired): split k stores this split's raw sums
+// to the partial buffer; f32 output goes straight from the accumulators; bf16 output is
+// scaled, staged through the ring as TM rows of 512 bytes and stored row by row.
+template <int TN, int TM>
+__device__ __forceinline__ void ring_epilogue(const GemmArgs& g, v16f (&acc)[TN / 64][TM / 128], int64_t m0,
+                                              int64_t n0, int ks, uint8_t* smem, int t, int wn, int wm, int r32,
+                                              int q) {
+    constexpr int kNI = TN / 64, kJX = TM / 128;
     // acc[i][jx] register r: n = 32 i + 8 (r / 4) + 4 q + r % 4, m = 32 jx + lane % 32 (wave
     // tile relative). The scaled bf16 tile is staged in LDS as [m][n] with 512-byte rows, the
     // 16-byte chunk cn of row ml at slot cn ^ (ml & 15) with its two 8-byte halves swapped when
@@ -625,6 +526,238 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     }
 }
 
+// Operands under 2^31 bytes (buffer offsets). Grid = number of TN x TM tiles, 512 threads.
+template <int TN, int TM>
+__global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
+    using RS = RingShape<TN, TM>;
+    constexpr int kStage = RS::kStage, kRing = RS::kRing, kNI = RS::kNI, kJX = RS::kJX, kLoads = RS::kLoads;
+    constexpr int kWStageT = TN * kWK;              // the weight rows' part of a stage
+    static_assert(TN == 256 && (TM == 256 || TM == 128), "tile shape");
+    static_assert(kRing >= 4 && (kRing - 2) * kLoads < 64, "ring depth and the vmcnt field");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
+    // the epilogue stages the bf16 tile in the ring as TM rows of 512 bytes (TN <= 256)
+    static_assert(kRing * kStage >= TM * 512, "the epilogue stages the whole bf16 tile in the ring");
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n TN / 2 x m TM / 4
+    const int r32 = lane & 31, q = lane >> 5;
+
+    int64_t m0, n0;
+    int ks;
+    ring_tile<TN, TM>(g, m0, n0, ks);
+
+    // DMA: wave w fills weight rows 32 w .. 32 w + 31 and activation rows (TM / 8) w ..
+    // (TM / 8) (w + 1) - 1 of a stage. 16 rows per instruction;
+    // lane l lands in slot l of the instruction's 1 KB: row 16 i + l / 4, chunk slot l % 4,
+    // which holds the logical chunk kc / 16 under the swizzle (the swizzle depends on the row
+    // modulo 16 only).
+    const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
+    const int lr = lane >> 2;
+    const int kc = ((lane & 3) ^ (((lr >> 1) ^ (lr >> 2)) & 3)) * 16;
+    uint32_t dbase[kLoads];    // this lane's source offset of each of the wave's blocks (k = 0)
+    int dlds[kLoads];          // the block's byte offset in a stage
+    bool dw[kLoads];           // weight block (else activation)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int blk = i < 2 ? wave * 2 + i : RS::kBlocks - TM / 16 + wave * kJX + (i - 2);
+        dw[i] = blk < TN / 16;
+        dlds[i] = blk * 1024;
+        if (dw[i]) {
+            const int row = blk * 16 + lr;
+            dbase[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
+        } else {
+            const int row = (blk - TN / 16) * 16 + lr;
+            dbase[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
+        }
+    }
+    // this block's k stages: s_beg .. s_beg + nk - 1 (all of k without a split)
+    const int nk_all = (int)((g.k + kWK - 1) / kWK);
+    const int kper = (nk_all + g.ksplit - 1) / g.ksplit;
+    const int s_beg = ks * kper;
+    const int nk = min(kper, nk_all - s_beg);   // >= 1: the launcher leaves no split empty
+    auto issue = [&](int s) {   // stage s (past k its loads are out of range, zeros; past this
+                                // split's range they are loaded and never read)
+        const uint32_t k0 = (uint32_t)(s_beg + s) * kWK;
+        const bool kin = (int64_t)k0 + kc < g.k;
+        uint8_t* sb = smem + (s % kRing) * kStage;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) dma16(dw[i] ? wrs : ars, sb + dlds[i], kin ? dbase[i] + k0 : kOutOfRange);
+    };
+    auto read_ops = [&](int s, v8i (&wop)[kNI], v8i (&aop)[kJX]) {
+        const uint8_t* sw = smem + (s % kRing) * kStage;
+        const uint8_t* sa = sw + kWStageT;
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+            const int row = wn * (TN / 2) + i * 32 + r32;
+            wop[i] = cat8(lds16(sw + swz64(row, 2 * q)), lds16(sw + swz64(row, 2 * q + 1)));
+        }
+#pragma unroll
+        for (int jx = 0; jx < kJX; ++jx) {
+            const int row = wm * (TM / 4) + jx * 32 + r32;
+            aop[jx] = cat8(lds16(sa + swz64(row, 2 * q)), lds16(sa + swz64(row, 2 * q + 1)));
+        }
+    };
+
+    v16f acc[kNI][kJX];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+#pragma unroll
+        for (int jx = 0; jx < kJX; ++jx)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
+
+    // Step kt: wait for stage kt + 1 (this thread's loads), barrier (all of them landed, and
+    // every wave is past step kt - 1, so the slot of stage kt - 1 is free), refill that slot
+    // with stage kt + kRing - 1, then read the operands of stage kt + 1 while the MFMAs of
+    // stage kt (read one step earlier) run.
+    auto step = [&](int kt, const v8i (&cw)[kNI], const v8i (&ca)[kJX], v8i (&nw)[kNI], v8i (&na)[kJX]) {
+        wait_vmcnt<(kRing - 3) * kLoads>();
+        __syncthreads();
+        issue(kt + kRing - 1);
+        if (kt + 1 < nk) read_ops(kt + 1, nw, na);
+        __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs
+#pragma unroll
+        for (int i = 0; i < kNI; ++i)
+#pragma unroll
+            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
+        __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
+    };
+#pragma unroll
+    for (int s = 0; s < kRing - 1; ++s) issue(s);
+    v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
+    wait_vmcnt<(kRing - 2) * kLoads>();
+    __syncthreads();
+    read_ops(0, w0, a0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, w0, a0, w1, a1);
+        step(kt + 1, w1, a1, w0, a0);
+    }
+    if (kt < nk) step(kt, w0, a0, w1, a1);
+    wait_vmcnt<0>();   // the ring's trailing loads (past k) before the ring is reused
+
+    ring_epilogue<TN, TM>(g, acc, m0, n0, ks, smem, t, wn, wm, r32, q);
+}
+
+// 128-byte LDS rows: chunk c of row r sits at slot c ^ (r & 7) ^ ((r >> 3) & 1). A b128 read
+// serves 16 lanes per pass; 16 consecutive rows read at one chunk land on 16 distinct 16-byte
+// units of the 256-byte bank window (rows of one parity differ in the slot's low bits, the two
+// parities sit 64 bytes apart, and bit 3 of the row flips the slot's lowest bit).
+__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7) ^ ((row >> 3) & 1)) << 4); }
+
+// The ring tile kernel with 128-byte k-stages: a stage holds 128 bytes of k for each of the
+// TN + TM rows, so every DMA request is a whole 128-byte line (the 64-byte stages issue half
+// lines) and a CU's requests in flight carry twice the bytes. A DMA block is 8 rows (1 KB);
+// each stage runs two MFMA k-steps. 192 x 128 only: four 40 KB stages fit the LDS.
+template <int TN, int TM>
+__global__ __launch_bounds__(512) void ring128_kernel(const GemmArgs g) {
+    constexpr int kK = 128;                              // k bytes per stage
+    constexpr int kStage = (TN + TM) * kK;
+    constexpr int kRing = (160 * 1024) / kStage;
+    constexpr int kNI = TN / 64, kJX = TM / 128;
+    constexpr int kBlocks = (TN + TM) / 8;
+    constexpr int kLoads = kBlocks / 8;                  // DMA instructions per wave per stage
+    static_assert(TN == 192 && TM == 128, "tile shape");
+    static_assert(kBlocks % 8 == 0 && kRing >= 4 && (kRing - 2) * kLoads < 64, "ring depth and the vmcnt field");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
+    static_assert(kRing * kStage >= TM * 512, "the epilogue stages the whole bf16 tile in the ring");
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wn = wave >> 2, wm = wave & 3;        // wave tile: n TN / 2 x m TM / 4
+    const int r32 = lane & 31, q = lane >> 5;
+    int64_t m0, n0;
+    int ks;
+    ring_tile<TN, TM>(g, m0, n0, ks);
+
+    // DMA: wave w takes the 8-row blocks w + 8 i of a stage (weight blocks first); lane l lands
+    // in slot l of the instruction's 1 KB: row 8 b + l / 8, slot l % 8, which holds the logical
+    // chunk kc / 16 under swz128 (the block's parity is bit 3 of its rows).
+    const i32x4 wrs = buffer_desc(g.w, g.n * g.k), ars = buffer_desc(g.a, g.m * g.lda);
+    const int lr = lane >> 3;
+    uint32_t dbase[kLoads];
+    int dlds[kLoads], dkc[kLoads];
+    bool dw[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int blk = wave + 8 * i;
+        dw[i] = blk < TN / 8;
+        dlds[i] = blk * 1024;
+        const int row = (dw[i] ? blk : blk - TN / 8) * 8 + lr;    // within the weight or activation rows
+        const int kc = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 16;
+        dkc[i] = kc;
+        if (dw[i])
+            dbase[i] = n0 + row < g.n ? (uint32_t)((n0 + row) * g.k + kc) : kOutOfRange;
+        else
+            dbase[i] = m0 + row < g.m ? (uint32_t)((m0 + row) * g.lda + kc) : kOutOfRange;
+    }
+    const int nk_all = (int)((g.k + kK - 1) / kK);
+    const int kper = (nk_all + g.ksplit - 1) / g.ksplit;
+    const int s_beg = ks * kper;
+    const int nk = min(kper, nk_all - s_beg);   // >= 1: the launcher leaves no split empty
+    auto issue = [&](int s) {   // stage s (past k: zeros; past this split's range: loaded, never read)
+        const uint32_t k0 = (uint32_t)(s_beg + s) * kK;
+        uint8_t* sb = smem + (s % kRing) * kStage;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i)
+            dma16(dw[i] ? wrs : ars, sb + dlds[i], (int64_t)k0 + dkc[i] < g.k ? dbase[i] + k0 : kOutOfRange);
+    };
+    auto read_ops = [&](int s, int h, v8i (&wop)[kNI], v8i (&aop)[kJX]) {   // k-step h of stage s
+        const uint8_t* sw = smem + (s % kRing) * kStage;
+        const uint8_t* sa = sw + TN * kK;
+        const int c0 = 4 * h + 2 * q;
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+            const int row = wn * (TN / 2) + i * 32 + r32;
+            wop[i] = cat8(lds16(sw + swz128(row, c0)), lds16(sw + swz128(row, c0 + 1)));
+        }
+#pragma unroll
+        for (int jx = 0; jx < kJX; ++jx) {
+            const int row = wm * (TM / 4) + jx * 32 + r32;
+            aop[jx] = cat8(lds16(sa + swz128(row, c0)), lds16(sa + swz128(row, c0 + 1)));
+        }
+    };
+
+    v16f acc[kNI][kJX];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+#pragma unroll
+        for (int jx = 0; jx < kJX; ++jx)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
+    auto mfmas = [&](const v8i (&cw)[kNI], const v8i (&ca)[kJX]) {
+#pragma unroll
+        for (int i = 0; i < kNI; ++i)
+#pragma unroll
+            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
+    };
+
+    // Stage s: its second k-step's operands are read (the stage has landed) while the first
+    // k-step's MFMAs run; then wait for stage s + 1 (this thread's loads), barrier (all of them
+    // landed, and every wave is done reading stage s - 1, whose slot is refilled with stage
+    // s + kRing - 1), read stage s + 1's first k-step and run the second k-step's MFMAs.
+#pragma unroll
+    for (int s = 0; s < kRing - 1; ++s) issue(s);
+    v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
+    wait_vmcnt<(kRing - 2) * kLoads>();
+    __syncthreads();
+    read_ops(0, 0, w0, a0);
+    for (int s = 0; s < nk; ++s) {
+        read_ops(s, 1, w1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(w0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(kRing - 3) * kLoads>();
+        __syncthreads();
+        issue(s + kRing - 1);
+        if (s + 1 < nk) read_ops(s + 1, 0, w0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(w1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();   // the ring's trailing loads (past k) before the ring is reused
+    ring_epilogue<TN, TM>(g, acc, m0, n0, ks, smem, t, wn, wm, r32, q);
+}
+
 // Split-k epilogue: out[m, n] = (sum over s of part[s, m, n], in split order) * a_scale *
 // w_scale[n], rounded once (bf16) or stored as f32. Four consecutive outputs per thread.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
@@ -680,8 +813,9 @@ static void launch_panel(const GemmArgs& g, hipStream_t st) {
 }
 
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
-// 192 x 128 ring tile (216 workgroups of 860 KB) takes in_proj to 25.4 us, against 28.6 for
-// 256 x 128 (164 of 1 MB) and 30.4 for a 128 x 192 panel kernel (two k-steps of register
+// 192 x 128 ring tile (216 workgroups of 860 KB) takes in_proj to 25.4 us with 64-byte
+// k-slices and 23.5 us with 128-byte ones (384 x 10300 x 2608: 34.3 vs 28.6 us), against 28.6
+// for 256 x 128 (164 of 1 MB) and 30.4 for a 128 x 192 panel kernel (two k-steps of register
 // prefetch); earlier panel versions took it from 37 to 33 us; where those
 // tiles give too few workgroups to fill the chip (out_proj: 56), 64 x 128 tiles
 // (168 workgroups) take it from 34 to 21 us. The 256 x 256 kernel leads from about
@@ -703,7 +837,8 @@ static int split_k(int64_t m, int64_t n, int64_t k) {
     const int64_t half_tiles = ((n + kWT - 1) / kWT) * ((m + 127) / 128);
     const int64_t t192 = ((n + 191) / 192) * ((m + 127) / 128);
     if (half_tiles >= 160 || t192 >= 160) return 1;
-    const int64_t nk = (k + kWK - 1) / kWK;
+    constexpr int64_t kSK = 128;   // k bytes per stage of the split kernel (ring128_kernel)
+    const int64_t nk = (k + kSK - 1) / kSK;
     const int64_t panel_wgs = 8 * ((m + 63) / 64) * (((n + 127) / 128 + 7) / 8);
     if (panel_wgs > 32) return 1;
     int64_t best = (panel_wgs + 255) / 256 * (64 + 128) * k;
@@ -711,7 +846,7 @@ static int split_k(int64_t m, int64_t n, int64_t k) {
     for (int S = 2; S <= 8; ++S) {
         const int64_t kper = (nk + S - 1) / S;
         if (kper * (S - 1) >= nk) continue;   // a split would be empty
-        const int64_t cost = (t192 * S + 255) / 256 * ((192 + 128) * kper * kWK + 4 * 192 * 128) +
+        const int64_t cost = (t192 * S + 255) / 256 * ((192 + 128) * kper * kSK + 4 * 192 * 128) +
                              S * m * n * 4 / 77 + 230000;
         if (cost < best) { best = cost; split = S; }
     }
@@ -741,7 +876,7 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         const int64_t c256 = half_tiles >= 160 ? ((half_tiles + 255) / 256) * (256 + 128) : INT64_MAX;
         const int64_t c192 = t192 >= 160 ? ((t192 + 255) / 256) * (192 + 128) : INT64_MAX;
         if (c192 < c256) {
-            tile256_kernel<192, 128><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
+            ring128_kernel<192, 128><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
             return check_launch("gemm (192 x 128)");
         }
         tile256_kernel<256, 128><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
@@ -752,7 +887,7 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         if (S > 1 && part && part_bytes >= gemm_part_bytes(m, n, k) && (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
             g.ksplit = S;
             g.part = part;
-            tile256_kernel<192, 128><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
+            ring128_kernel<192, 128><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
             nhm_status s = check_launch("gemm (192 x 128, split k)");
             if (s != NHM_OK) return s;
             splitk_reduce_kernel<<<dim3((unsigned)((m * n + 1023) / 1024)), dim3(256), 0, st>>>(g);
