@@ -124,8 +124,10 @@ def test_decode_one_block_one_token(nhm, block0):
     print(f"decode m=1: {m}, state rel l2 {st:.3e}")
 
 
+# 20: in_proj and out_proj one GEMV per 16 rows; 33 and 64: out_proj as one GEMM call with
+# split k (33: ragged m), in_proj still per 16 rows; 64 is the whole 64-slot pool in one call
 @pytest.mark.parametrize("B,slot_list,S", [(8, None, 24), (3, [5, -1, 0], 24), (20, None, 24),
-                                           (64, None, 64)])        # the whole 64-slot pool in one call
+                                           (33, None, 48), (64, None, 64)])
 def test_decode_batch(nhm, block0, B, slot_list, S):
     from oracle import mixer_decode
     from tests.gpu_util import upload_params, ws_region
