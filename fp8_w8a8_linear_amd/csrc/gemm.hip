@@ -350,7 +350,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWT = 256;               // workgroup tile extent in n (and in m for the square tile)
 constexpr int kWK = 64;                // k bytes per ring stage (one 32x32x64 MFMA deep)
-constexpr int kWStage = kWT * kWK;     // the weight tile's part of a stage, 16 KB
 
 // Ring geometry of a TN (n) x TM (m) tile with 64-byte k-slices: a stage holds TN weight rows
 // then TM activation rows of 64 bytes; as many stages as fit the 160 KB LDS (5 x 32 KB for
