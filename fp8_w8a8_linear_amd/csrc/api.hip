@@ -38,6 +38,10 @@ static nhm_status check_geometry(const nhm_geometry* g) {
                     g->head_dim, g->d_state, g->conv_width);
     if (g->n_heads % g->n_groups != 0)
         return fail(NHM_ERR_UNSUPPORTED, "n_heads %d is not a multiple of n_groups %d", g->n_heads, g->n_groups);
+    // in_proj rows are d_in_proj = 64 n_heads + conv_dim + n_heads bf16 wide and are read
+    // 16 bytes at a time, which needs d_in_proj % 8 == 0, i.e. n_heads % 8 == 0
+    if (g->n_heads % 8 != 0)
+        return fail(NHM_ERR_UNSUPPORTED, "n_heads %d must be a multiple of 8 (16-byte in_proj rows)", g->n_heads);
     if (g->hidden % 16 != 0 || g->hidden > 16384)
         return fail(NHM_ERR_UNSUPPORTED, "hidden %d must be a multiple of 16 and at most 16384", g->hidden);
     if (!(g->rms_eps > 0.f) || !isfinite(g->rms_eps))
@@ -83,6 +87,15 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
 // The weight-streaming GEMV serves m <= 16 (k up to 16384, weights under 2 GiB: its buffer
 // descriptors take 32-bit offsets); the tiled GEMM the rest.
 static bool use_gemv(int64_t m, int64_t n, int64_t k) { return m <= 16 && k <= 16384 && n * k < (int64_t(1) << 31); }
+
+// Every kernel addresses its operands through buffer descriptors with 32-bit offsets: an
+// operand of 2 GiB or more is refused on the host before anything is enqueued.
+static nhm_status check_offsets(int64_t m, int64_t lda, int64_t n, int64_t k, const char* what) {
+    if (n * k >= (int64_t(1) << 31) || m * lda >= (int64_t(1) << 31))
+        return fail(NHM_ERR_UNSUPPORTED, "%s: an operand of 2 GiB or more ([%lld, %lld] weight, %lld x %lld activation)",
+                    what, (long long)n, (long long)k, (long long)m, (long long)lda);
+    return NHM_OK;
+}
 
 // Split-k partials of one projection: none where the GEMV runs.
 static size_t proj_part_bytes(int64_t m, int64_t n, int64_t k) { return use_gemv(m, n, k) ? 0 : gemm_part_bytes(m, n, k); }
@@ -271,6 +284,7 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (ws && !aligned(ws, 256)) return fail(NHM_ERR_ALIGN, "ws must be 256-byte aligned");
+    if ((s = check_offsets(m, a_type == NHM_BF16 ? w->k : ld_a, w->n, w->k, "linear")) != NHM_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* aq = static_cast<const uint8_t*>(a);
     int64_t lda = ld_a;
@@ -340,6 +354,9 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     const MixerWs w = decode_ws(&p->g, batch);
     if (ws_bytes < w.pub.total)
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
+    if ((s = check_offsets(batch, p->g.hidden, l.d_in_proj, p->g.hidden, "decode in_proj")) != NHM_OK ||
+        (s = check_offsets(batch, l.d_inner, p->g.hidden, l.d_inner, "decode out_proj")) != NHM_OK)
+        return s;
     hipStream_t st = (hipStream_t)stream;
     char* wsb = static_cast<char*>(ws);
     const int64_t H = p->g.hidden;
@@ -443,6 +460,9 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
     if ((int64_t)w.max_chunks * p->g.n_heads > INT32_MAX)   // one scan block per (chunk, head)
         return fail(NHM_ERR_UNSUPPORTED, "%d chunks x %d heads exceed the scan's grid", w.max_chunks, p->g.n_heads);
+    if ((s = check_offsets(n_tokens, p->g.hidden, l.d_in_proj, p->g.hidden, "prefill in_proj")) != NHM_OK ||
+        (s = check_offsets(n_tokens, l.d_inner, p->g.hidden, l.d_inner, "prefill out_proj")) != NHM_OK)
+        return s;
     hipStream_t st = (hipStream_t)stream;
     char* wsb = static_cast<char*>(ws);
     const int64_t H = p->g.hidden;
@@ -460,8 +480,6 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     // token's decay exponentiates: its columns are recomputed with exact f32 accumulation in
     // the conv launch (the GEMV that serves small m accumulates exactly already)
     a.exact = n_tokens > 0 && !use_gemv(n_tokens, p->in_proj.n, p->in_proj.k);
-    if (a.exact && (p->in_proj.n * p->in_proj.k >= (int64_t(1) << 31) || n_tokens * H >= (int64_t(1) << 31)))
-        return fail(NHM_ERR_UNSUPPORTED, "prefill dt recompute: operands of 2 GiB or more");
     a.q_in = q_in;
     a.in_w = p->in_proj.w;
     a.in_w_scale = p->in_proj.w_scale;

@@ -231,25 +231,17 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
 
 constexpr int kTile = 128;   // n, m and k extent of a workgroup tile
 
-// Loads this thread's four 16-byte chunks of a 128 x 128 operand tile: through a buffer
-// descriptor (kBuf: operand under 2 GiB; its range check zero-fills rows and k past the
-// end, so there are no branches around the loads) or through a pointer with guards.
-template <bool kBuf>
-__device__ __forceinline__ void load_tile(uint4 (&r)[4], const uint8_t* base, const __amdgpu_buffer_rsrc_t& rs,
-                                          int64_t ld, int64_t row0, int64_t nrows, int64_t k0, int64_t k) {
+// Loads this thread's four 16-byte chunks of a 128 x 128 operand tile through a buffer
+// descriptor (operands under 2 GiB): its range check zero-fills rows and k past the end,
+// so there are no branches around the loads.
+__device__ __forceinline__ void load_tile(uint4 (&r)[4], const __amdgpu_buffer_rsrc_t& rs, int64_t ld, int64_t row0,
+                                          int64_t nrows, int64_t k0, int64_t k) {
     const int t = threadIdx.x;
     const int64_t kb = k0 + (t & 7) * 16;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int64_t row = row0 + p * 32 + (t >> 3);
-        if constexpr (kBuf) {
-            r[p] = bload(rs, row < nrows && kb < k ? (uint32_t)(row * ld + kb) : kOutOfRange);
-        } else {
-            if (row < nrows && kb < k)
-                r[p] = *reinterpret_cast<const uint4*>(base + row * ld + kb);
-            else
-                r[p] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        r[p] = bload(rs, row < nrows && kb < k ? (uint32_t)(row * ld + kb) : kOutOfRange);
     }
 }
 
@@ -263,7 +255,6 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* s, int row, int q) {
     return cat8(*reinterpret_cast<const uint4*>(s + swz(row, 2 * q)), *reinterpret_cast<const uint4*>(s + swz(row, 2 * q + 1)));
 }
 
-template <bool kBuf>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sW[2][kTile * kTile];
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][kTile * kTile];
@@ -288,15 +279,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // (the descriptors are built either way; the pointer path never reads through them)
-    const int64_t imax = 0x7fffffff;
-    const __amdgpu_buffer_rsrc_t wrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k < imax ? g.n * g.k : imax), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ars =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda < imax ? g.m * g.lda : imax), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
     uint4 rw[4], ra[4];
-    load_tile<kBuf>(rw, g.w, wrs, g.k, n0, g.n, 0, g.k);
-    load_tile<kBuf>(ra, g.a, ars, g.lda, m0, g.m, 0, g.k);
+    load_tile(rw, wrs, g.k, n0, g.n, 0, g.k);
+    load_tile(ra, ars, g.lda, m0, g.m, 0, g.k);
     stage_tile(sW[0], rw);
     stage_tile(sA[0], ra);
     __syncthreads();
@@ -304,8 +291,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) {
-            load_tile<kBuf>(rw, g.w, wrs, g.k, n0, g.n, (int64_t)(kt + 1) * kTile, g.k);
-            load_tile<kBuf>(ra, g.a, ars, g.lda, m0, g.m, (int64_t)(kt + 1) * kTile, g.k);
+            load_tile(rw, wrs, g.k, n0, g.n, (int64_t)(kt + 1) * kTile, g.k);
+            load_tile(ra, ars, g.lda, m0, g.m, (int64_t)(kt + 1) * kTile, g.k);
         }
         v8i av[4], bv[4];
 #pragma unroll
@@ -900,11 +887,10 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         tile256_kernel<256, 256><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 256)");
     }
+    if (!offsets_fit)   // refused by the callers' host checks before anything is enqueued
+        return fail(NHM_ERR_UNSUPPORTED, "gemm: an operand of 2 GiB or more");
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));
-    if (offsets_fit)
-        gemm_kernel<true><<<grid, dim3(256), 0, st>>>(g);
-    else
-        gemm_kernel<false><<<grid, dim3(256), 0, st>>>(g);
+    gemm_kernel<<<grid, dim3(256), 0, st>>>(g);
     return check_launch("gemm");
 }
 

@@ -61,7 +61,10 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
 
 // E4M3(x / s) for positive scales in [2^-80, 2^100], without a division per element.
 // With r = 1/s rounded to nearest (one IEEE division per thread), q0 = RN(x r) is corrected
-// once by the exact residual: q = RN(q0 - RN(q0 s - x) r). This equals the IEEE quotient
+// once by the exact residual: q = RN(q0 - RN(q0 s - x) r) -- Markstein's correction step
+// for division by a known reciprocal (P. Markstein, "Computation of elementary functions on
+// the IBM RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990), whose residual
+// q0 s - x one fused multiply-add computes exactly. This equals the IEEE quotient
 // RN(x / s) bit for bit, signed zeros included: checked on the host's IEEE f32 arithmetic
 // (tests/c/recip_div_check.c) over every bf16 significand (both signs) against every f32
 // scale significand in [1, 2) (2^31 pairs; exponents only scale both sides inside this

@@ -64,7 +64,12 @@ typedef enum nhm_status {
 typedef enum nhm_dtype {
     NHM_BF16 = 0,            /* bfloat16 bit patterns (uint16_t)                   */
     NHM_E4M3 = 1,            /* OCP FP8 E4M3FN codes (uint8_t)                      */
-    NHM_F32 = 2              /* IEEE binary32 (float): GEMM output, SSM state       */
+    NHM_F32 = 2,             /* IEEE binary32 (float): GEMM output, SSM state       */
+    /* Not types: they make every 32-bit int a value of the enum, so that any integer a
+     * caller passes is well defined on the library side and reaches validation
+     * (NHM_ERR_UNSUPPORTED). */
+    NHM_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    NHM_DTYPE_RANGE_MAX_ = 2147483647
 } nhm_dtype;
 
 /* Static name of a status code. Never NULL. */
@@ -82,7 +87,8 @@ NHM_API const char* nhm_build_arch(void);
 /* Mixer geometry. [PR1288] opening section (2688 -> 10304 in_proj, 4096 -> 2688
  * out_proj); [PR950] "Review repairs" F2 (64 heads; three f32 per-head SSM
  * tensors). Supported by the kernels: head_dim == 64, d_state == 128,
- * conv_width == 4, n_heads % n_groups == 0, hidden % 16 == 0, 0 < rms_eps
+ * conv_width == 4, n_heads % n_groups == 0, n_heads % 8 == 0 (in_proj rows are
+ * read 16 bytes at a time), hidden % 16 == 0, 0 < rms_eps
  * (an eps of 0 is refused: [PR950] "Not dense_attn::AttnBlock (#941)" reports a
  * missing rms eps key silently becoming 0). */
 typedef struct nhm_geometry {
@@ -95,10 +101,10 @@ typedef struct nhm_geometry {
     float rms_eps;       /* gated RMSNorm epsilon (1e-5), > 0           */
 } nhm_geometry;
 
-/* Split indices of one in_proj row and of the conv output.
- * [PR1289] commit log: the first split has three outputs of widths
- * (I, conv_dim, num_heads) taking the head, middle and tail of an in_proj row;
- * [PR1288] "What it does": the second split is x | B | C. */
+/* Split indices of one in_proj row and of the conv output ([PR1289] commit log;
+ * [PR1288] "What it does"). An in_proj row is z, then xBC, then dt: three adjacent
+ * column ranges of widths I, conv_dim and n_heads. The conv output row is x, then B,
+ * then C. */
 typedef struct nhm_layout {
     int32_t d_inner;          /* I = n_heads * head_dim                      */
     int32_t conv_dim;         /* I + 2 * n_groups * d_state                  */
@@ -191,7 +197,11 @@ NHM_API size_t nhm_fp8_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, n
  * their f32 partial sums are added in split order by a second kernel, then scaled and
  * rounded once.
  * Results are deterministic (no atomics).
- * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
+ * Every kernel addresses its operands with 32-bit offsets: a weight (n * k) or an activation
+ * (m * ld_a, or m * k for a bf16 input's codes) of 2 GiB or more is NHM_ERR_UNSUPPORTED,
+ * refused before anything is enqueued.
+ * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED, NHM_ERR_WORKSPACE,
+ * NHM_ERR_HIP. */
 NHM_API nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
                           const nhm_fp8_weight* w, uint16_t* out, int64_t ld_out,
                           void* ws, size_t ws_bytes, void* stream);
@@ -258,7 +268,7 @@ NHM_API nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t bat
  *   out       (device) bf16 [batch, g.hidden]; must not overlap hidden
  *   ws        (device) >= nhm_mixer_decode_ws_layout(g, batch).total bytes
  * Both projections run as the exact-f32 GEMV of nhm_fp8_linear, 16 rows at a time
- * (a geometry whose in_proj weight reaches 2 GiB is NHM_ERR_UNSUPPORTED).
+ * (a weight or activation of 2 GiB or more is NHM_ERR_UNSUPPORTED, as in nhm_fp8_linear).
  * batch == 0 is a valid no-op.
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
  * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
@@ -295,7 +305,8 @@ NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_
  * recomputed with exact f32 accumulation.
  * n_tokens == 0 with n_seqs == 0 is a valid no-op. The scan runs one block per
  * (chunk, head): (n_tokens / chunk + n_seqs) * g.n_heads above 2^31 - 1 is
- * NHM_ERR_UNSUPPORTED.
+ * NHM_ERR_UNSUPPORTED, and so is a projection operand of 2 GiB or more (as in
+ * nhm_fp8_linear).
  * Errors: NHM_ERR_NULL, NHM_ERR_SHAPE, NHM_ERR_ALIGN, NHM_ERR_UNSUPPORTED,
  * NHM_ERR_WORKSPACE, NHM_ERR_HIP. */
 NHM_API nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,

@@ -72,10 +72,10 @@ GEOMETRY = dict(hidden=2688, n_heads=64, head_dim=64, d_state=128,
 def layout(g=GEOMETRY):
     """Column offsets of the two splits of one in_proj row.
 
-    [PR1289] commit log: the first split has three outputs of widths
-    (I, conv_dim, num_heads) that take the head, middle and tail of an in_proj
-    row; [PR1288] "What it does": the second split is x | B | C of the conv
-    output. I = n_heads*head_dim, conv_dim = I + 2*n_groups*d_state.
+    [PR1289] commit log and [PR1288] "What it does": an in_proj row is z, xBC
+    and dt as adjacent column ranges (widths I, conv_dim and n_heads, in that
+    order), and a conv output row is x, B and C in that order.
+    I = n_heads*head_dim, conv_dim = I + 2*n_groups*d_state.
     """
     inner = g["n_heads"] * g["head_dim"]
     gs = g["n_groups"] * g["d_state"]

@@ -49,6 +49,17 @@ def test_unsupported_geometry(nhm, field, value):
     assert e.value.status == 4
 
 
+def test_n_heads_not_multiple_of_8_refused(nhm):
+    """in_proj rows (64 n_heads + conv_dim + n_heads bf16) are read 16 bytes at a time, so
+    n_heads must be a multiple of 8 even where n_groups divides it."""
+    for nh, ng in [(4, 2), (12, 4), (20, 4)]:
+        g = dict(nhm.GEOMETRY, n_heads=nh, n_groups=ng, hidden=256)
+        with pytest.raises(nhm.NhmError) as e:
+            nhm.mixer_layout(g)
+        assert e.value.status == 4 and b"multiple of 8" in nhm.lib.nhm_last_error()
+    assert nhm.mixer_layout(dict(nhm.GEOMETRY, n_heads=8, n_groups=2, hidden=256))["d_in_proj"] % 8 == 0
+
+
 def _w(nhm, w=0x1000, s=0x2000, a=0x3000, n=64, k=128):
     return nhm._Fp8Weight(w, s, a, n, k)
 
@@ -92,6 +103,23 @@ def test_linear_ex_refusals(nhm):
         assert st == status, (over, st, nhm.lib.nhm_last_error())
     # a bf16 output only needs 2-byte alignment, as in nhm_fp8_linear
     assert ex(A, nhm.NHM_BF16, 0, 128, C.byref(w), O + 2, nhm.NHM_BF16, 64, WS, need, None) == 0
+
+
+def test_linear_two_gib_operands_refused(nhm):
+    """Operands of 2 GiB or more (32-bit buffer offsets) are refused on the host, before the
+    quant of a bf16 input is enqueued, on the GEMV (m <= 16) and the tiled (m > 16) paths."""
+    A, O, WS = 0x10000, 0x20000, 0x40000
+    # (m, n, k, ld_a, input types): every case is refused (a bf16 input with a wide row
+    # stride is quantized into [m, k] codes first, so only its e4m3 form is refused there)
+    cases = [(8, 1 << 19, 4096, 4096, (nhm.NHM_BF16, nhm.NHM_E4M3)),
+             (32, 1 << 19, 4096, 4096, (nhm.NHM_BF16, nhm.NHM_E4M3)),
+             (1 << 19, 64, 4096, 4096, (nhm.NHM_BF16, nhm.NHM_E4M3)),
+             (32, 64, 128, 1 << 26, (nhm.NHM_E4M3,))]
+    for m, n, k, ld, types in cases:
+        for a_type in types:
+            st = _lin(nhm, A, a_type, m, ld, _w(nhm, n=n, k=k), O, n, WS, 1 << 62)
+            assert st == 4, (m, n, k, ld, a_type, st, nhm.lib.nhm_last_error())
+            assert b"2 GiB" in nhm.lib.nhm_last_error()
 
 
 def test_linear_zero_rows_is_noop(nhm):
