@@ -69,6 +69,8 @@ _SIGS = {
     "nhm_fp8_dequant_channel_bf16": (C.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     "nhm_fp8_linear": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, _i64, _p, _sz, _p]),
     "nhm_fp8_linear_ex": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, C.c_int, _i64, _p, _sz, _p]),
+    "nhm_fp8_linear_exact": (C.c_int, [_p, C.c_int, _i64, _i64, C.POINTER(_Fp8Weight), _p, C.c_int, _i64, _p, _sz,
+                                       _p]),
     "nhm_mixer_decode_ws_layout": (C.c_int, [C.POINTER(Geometry), _i32, C.POINTER(WsLayout)]),
     "nhm_mixer_prefill_ws_layout": (C.c_int, [C.POINTER(Geometry), _i64, _i32, _i32, C.POINTER(WsLayout)]),
     "nhm_mixer_decode": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p]),
@@ -171,10 +173,11 @@ def fp8_linear_workspace_bytes(m, n, k, a_type):
     return int(lib.nhm_fp8_linear_workspace_bytes(m, n, k, a_type))
 
 
-def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None, out_type=None):
+def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None, out_type=None, exact=False):
     """[m, n] = W8A8(a [m, k], weight). a: bf16 bits (int16/uint16/bfloat16) or e4m3 codes (uint8).
 
-    The output is bf16 bits (int16) unless out_type is NHM_F32 (or out is a float32 tensor)."""
+    The output is bf16 bits (int16) unless out_type is NHM_F32 (or out is a float32 tensor).
+    exact=True calls nhm_fp8_linear_exact (every product summed in f32 on every path)."""
     import torch
     a = _dev_tensor(a, "a")
     if a_type is None:
@@ -187,8 +190,9 @@ def fp8_linear(a, weight: Fp8Weight, out=None, ws=None, a_type=None, stream=None
     need = fp8_linear_workspace_bytes(m, weight.n, weight.k, a_type)
     if ws is None and need > 0:
         ws = torch.zeros(need, dtype=torch.uint8, device=a.device)
-    _check(lib.nhm_fp8_linear_ex(_ptr(a), a_type, m, a.shape[1], C.byref(weight.struct), _ptr(out), out_type,
-                                 out.shape[1], _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    fn = lib.nhm_fp8_linear_exact if exact else lib.nhm_fp8_linear_ex
+    _check(fn(_ptr(a), a_type, m, a.shape[1], C.byref(weight.struct), _ptr(out), out_type, out.shape[1], _ptr(ws),
+              0 if ws is None else ws.numel(), _stream(stream)))
     return out
 
 

@@ -164,12 +164,14 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
 
 // One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
 // part / part_bytes: scratch for the GEMM's split-k partials (nullptr: no split).
+// exact: every product summed in f32 on the tiled path too (the GEMV always is).
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
                           int64_t ld_out, hipStream_t st, float* out_f32 = nullptr, float* part = nullptr,
-                          size_t part_bytes = 0) {
+                          size_t part_bytes = 0, bool exact = false) {
     if (use_gemv(m, w.n, w.k))
         return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
-    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, part, part_bytes);
+    return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, part, part_bytes,
+                       exact);
 }
 
 static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
@@ -258,8 +260,9 @@ nhm_status nhm_fp8_linear(const void* a, nhm_dtype a_type, int64_t m, int64_t ld
     return nhm_fp8_linear_ex(a, a_type, m, ld_a, w, out, NHM_BF16, ld_out, ws, ws_bytes, stream);
 }
 
-nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
-                             void* out, nhm_dtype out_type, int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+static nhm_status linear_call(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
+                              void* out, nhm_dtype out_type, int64_t ld_out, void* ws, size_t ws_bytes, void* stream,
+                              bool exact) {
     g_err[0] = 0;
     if (out_type != NHM_BF16 && out_type != NHM_F32)
         return fail(NHM_ERR_UNSUPPORTED, "output dtype %d: bf16 or f32", (int)out_type);
@@ -300,8 +303,19 @@ nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t
     const size_t pb = proj_part_bytes(m, w->n, w->k);
     float* part = pb > 0 && ws && ws_bytes >= need + pb ? reinterpret_cast<float*>(wsb + need) : nullptr;
     if (out_type == NHM_F32)
-        return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out), part, part ? pb : 0);
-    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, st, nullptr, part, part ? pb : 0);
+        return project(aq, lda, m, *w, nullptr, ld_out, st, static_cast<float*>(out), part, part ? pb : 0, exact);
+    return project(aq, lda, m, *w, static_cast<uint16_t*>(out), ld_out, st, nullptr, part, part ? pb : 0, exact);
+}
+
+nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
+                             void* out, nhm_dtype out_type, int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+    return linear_call(a, a_type, m, ld_a, w, out, out_type, ld_out, ws, ws_bytes, stream, false);
+}
+
+nhm_status nhm_fp8_linear_exact(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a, const nhm_fp8_weight* w,
+                                void* out, nhm_dtype out_type, int64_t ld_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+    return linear_call(a, a_type, m, ld_a, w, out, out_type, ld_out, ws, ws_bytes, stream, true);
 }
 
 nhm_status nhm_mixer_decode_ws_layout(const nhm_geometry* g, int32_t batch, nhm_ws_layout* out) {
@@ -471,20 +485,14 @@ nhm_status nhm_mixer_prefill_ex(const nhm_mixer_params* p, const uint16_t* hidde
     if (n_tokens > 0) {
         launch_quantize(hidden, n_tokens, H, H, p->in_proj.a_scale, q_in, H, st);
         if ((s = check_launch("prefill quant")) != NHM_OK) return s;
+        // every product summed in f32: the e4m3 MFMA's coarser 128-product sums move about 1 %
+        // of the bf16 projection outputs by one step, and those steps reach the a9 codes through
+        // dt (exponentiated by every later token's decay), x, B, C and the gate
         if ((s = project(q_in, H, n_tokens, p->in_proj, zx, l.d_in_proj, st, nullptr,
-                         reinterpret_cast<float*>(wsb + w.part), w.part_bytes)) != NHM_OK)
+                         reinterpret_cast<float*>(wsb + w.part), w.part_bytes, true)) != NHM_OK)
             return s;
     }
     PrefillArgs a;
-    // the e4m3 GEMM's coarse sum is harmless for z and xBC but not for dt, which every later
-    // token's decay exponentiates: its columns are recomputed with exact f32 accumulation in
-    // the conv launch (the GEMV that serves small m accumulates exactly already)
-    a.exact = n_tokens > 0 && !use_gemv(n_tokens, p->in_proj.n, p->in_proj.k);
-    a.q_in = q_in;
-    a.in_w = p->in_proj.w;
-    a.in_w_scale = p->in_proj.w_scale;
-    a.in_a_scale = p->in_proj.a_scale;
-    a.hidden = p->g.hidden;
     a.T = n_tokens;
     a.n_seqs = n_seqs;
     a.chunk = chunk;

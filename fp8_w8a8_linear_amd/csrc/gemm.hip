@@ -90,6 +90,24 @@ __device__ __forceinline__ void store_tile_f32(float* out, int64_t ld_out, int64
     }
 }
 
+// One 128-deep k-step of a 16 x 16 tile. kExact == false: the e4m3 MFMA, whose 128-product
+// reductions are coarser than f32. kExact: every product summed in f32 -- the lane's 32 code
+// bytes of each operand are split into four runs of eight (the same bytes of both operands
+// per run, so the four runs cover each product once), converted to bf16 (exact for every
+// e4m3 value) and summed by four bf16 MFMAs.
+template <bool kExact>
+__device__ __forceinline__ v4f mfma16_step(const v8i& a, const v8i& b, const v4f& c) {
+    if constexpr (!kExact) {
+        return mfma_e4m3(a, b, c);
+    } else {
+        v4f r = c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r = mfma_bf16(e4m3x8_to_bf16(a[2 * j], a[2 * j + 1]), e4m3x8_to_bf16(b[2 * j], b[2 * j + 1]), r);
+        return r;
+    }
+}
+
 // ---------------------------------------------------------------- panel kernel
 
 constexpr int kPanelDepth = 2;   // weight k-steps in flight per wave (and activation tiles in registers)
@@ -100,7 +118,7 @@ __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;   // past every buffer range used here (< 2^31 bytes)
 
-template <int BM, int WN>
+template <int BM, int WN, bool kExact>
 __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
     constexpr int BN = 4 * WN, TN = WN / 16, TM = BM / 16, D = kPanelDepth;
     constexpr int LA = BM * 8 / 256;   // 16-byte chunks of the activation tile per thread
@@ -200,7 +218,7 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
             for (int j = 0; j < TM; ++j)
 #pragma unroll
                 for (int i = 0; i < TN; ++i)
-                    acc[i][j] = mfma_e4m3(cat8(wr[u % D][i][0], wr[u % D][i][1]), bop[u & 1][j], acc[i][j]);
+                    acc[i][j] = mfma16_step<kExact>(cat8(wr[u % D][i][0], wr[u % D][i][1]), bop[u & 1][j], acc[i][j]);
             wload(kt + D, wr[u % D]);
             astore(b2, ar[(u + 2) % D]);
             aload(kt + 2 + D, ar[(u + 2) % D]);
@@ -255,6 +273,7 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* s, int row, int q) {
     return cat8(*reinterpret_cast<const uint4*>(s + swz(row, 2 * q)), *reinterpret_cast<const uint4*>(s + swz(row, 2 * q + 1)));
 }
 
+template <bool kExact>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sW[2][kTile * kTile];
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][kTile * kTile];
@@ -302,7 +321,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_e4m3(av[i], bv[j], acc[i][j]);
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_step<kExact>(av[i], bv[j], acc[i][j]);
         if (kt + 1 < nk) {
             stage_tile(sW[cur ^ 1], rw);
             stage_tile(sA[cur ^ 1], ra);
@@ -355,6 +374,42 @@ struct RingShape {
 
 __device__ __forceinline__ v16f mfma32_e4m3(const v8i& a, const v8i& b, const v16f& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32x32x16 bf16 MFMA, f32 accumulate: lane l supplies row (l % 32) of A and column (l % 32) of
+// B as 8 consecutive k of the 16-k step chosen by l / 32; the accumulator layout is that of
+// the 32x32x64 e4m3 MFMA.
+__device__ __forceinline__ v16f mfma32_bf16(const bf16x8& a, const bf16x8& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 64-deep k-step of a wave's NI x NJ grid of 32 x 32 tiles (weight fragments w, activation
+// fragments a; 32 code bytes per lane each). kExact == false: one e4m3 MFMA per tile. kExact:
+// every product summed in f32 -- run j of four takes bytes 8 j .. 8 j + 7 of every fragment
+// (the same k bytes of both operands), converts them to bf16 (exact for every e4m3 value; each
+// fragment once per run, not once per tile) and feeds one bf16 MFMA per tile; the tiles are
+// innermost, so consecutive MFMAs go to different accumulators.
+template <bool kExact, int NI, int NJ>
+__device__ __forceinline__ void mfma32_grid(v16f (&acc)[NI][NJ], const v8i (&w)[NI], const v8i (&a)[NJ]) {
+    if constexpr (!kExact) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int jx = 0; jx < NJ; ++jx) acc[i][jx] = mfma32_e4m3(w[i], a[jx], acc[i][jx]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8 wb[NI], ab[NJ];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) wb[i] = e4m3x8_to_bf16(w[i][2 * j], w[i][2 * j + 1]);
+#pragma unroll
+            for (int jx = 0; jx < NJ; ++jx) ab[jx] = e4m3x8_to_bf16(a[jx][2 * j], a[jx][2 * j + 1]);
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int jx = 0; jx < NJ; ++jx) acc[i][jx] = mfma32_bf16(wb[i], ab[jx], acc[i][jx]);
+        }
+    }
 }
 
 // Two floats to packed bf16 by the hardware conversion: round half to even, equal to
@@ -513,7 +568,7 @@ __device__ __forceinline__ void ring_epilogue(const GemmArgs& g, v16f (&acc)[TN 
 }
 
 // Operands under 2^31 bytes (buffer offsets). Grid = number of TN x TM tiles, 512 threads.
-template <int TN, int TM>
+template <int TN, int TM, bool kExact>
 __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     using RS = RingShape<TN, TM>;
     constexpr int kStage = RS::kStage, kRing = RS::kRing, kNI = RS::kNI, kJX = RS::kJX, kLoads = RS::kLoads;
@@ -602,10 +657,7 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
         issue(kt + kRing - 1);
         if (kt + 1 < nk) read_ops(kt + 1, nw, na);
         __builtin_amdgcn_sched_barrier(0);   // the reads go out before the MFMAs
-#pragma unroll
-        for (int i = 0; i < kNI; ++i)
-#pragma unroll
-            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
+        mfma32_grid<kExact>(acc, cw, ca);
         __builtin_amdgcn_sched_barrier(0);   // and the MFMAs before the next barrier
     };
 #pragma unroll
@@ -635,7 +687,7 @@ __device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^
 // TN + TM rows, so every DMA request is a whole 128-byte line (the 64-byte stages issue half
 // lines) and a CU's requests in flight carry twice the bytes. A DMA block is 8 rows (1 KB);
 // each stage runs two MFMA k-steps. 192 x 128 only: four 40 KB stages fit the LDS.
-template <int TN, int TM>
+template <int TN, int TM, bool kExact>
 __global__ __launch_bounds__(512) void ring128_kernel(const GemmArgs g) {
     constexpr int kK = 128;                              // k bytes per stage
     constexpr int kStage = (TN + TM) * kK;
@@ -710,12 +762,7 @@ __global__ __launch_bounds__(512) void ring128_kernel(const GemmArgs g) {
         for (int jx = 0; jx < kJX; ++jx)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
-    auto mfmas = [&](const v8i (&cw)[kNI], const v8i (&ca)[kJX]) {
-#pragma unroll
-        for (int i = 0; i < kNI; ++i)
-#pragma unroll
-            for (int jx = 0; jx < kJX; ++jx) acc[i][jx] = mfma32_e4m3(cw[i], ca[jx], acc[i][jx]);
-    };
+    auto mfmas = [&](const v8i (&cw)[kNI], const v8i (&ca)[kJX]) { mfma32_grid<kExact>(acc, cw, ca); };
 
     // Stage s: its second k-step's operands are read (the stage has landed) while the first
     // k-step's MFMAs run; then wait for stage s + 1 (this thread's loads), barrier (all of them
@@ -792,10 +839,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int BM, int WN>
+template <int BM, int WN, bool kExact>
 static void launch_panel(const GemmArgs& g, hipStream_t st) {
     const int64_t npan = (g.n + 4 * WN - 1) / (4 * WN), nmt = (g.m + BM - 1) / BM;
-    panel_kernel<BM, WN><<<dim3((unsigned)(8 * nmt * ((npan + 7) / 8))), dim3(256), 0, st>>>(g);
+    panel_kernel<BM, WN, kExact><<<dim3((unsigned)(8 * nmt * ((npan + 7) / 8))), dim3(256), 0, st>>>(g);
 }
 
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
@@ -844,13 +891,9 @@ size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k) {
     return S > 1 ? (size_t)S * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
-nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
-                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st, float* out_f32, float* part, size_t part_bytes) {
-    GemmArgs g{a, lda, m, w, w_scale, a_scale, n, k, out, ld_out,
-               out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
-                       : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0,
-               out_f32};
+template <bool kExact>
+static nhm_status dispatch_gemm(GemmArgs g, hipStream_t st, float* part, size_t part_bytes) {
+    const int64_t m = g.m, n = g.n, k = g.k, lda = g.lda;
     // buffer descriptors address the operands with 32-bit offsets
     const bool offsets_fit = n * k < (int64_t(1) << 31) && m * lda < (int64_t(1) << 31);
     // m <= 640: a ring tile when it gives >= 160 workgroups; of 256 x 128 and 192 x 128 the one
@@ -862,10 +905,10 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         const int64_t c256 = half_tiles >= 160 ? ((half_tiles + 255) / 256) * (256 + 128) : INT64_MAX;
         const int64_t c192 = t192 >= 160 ? ((t192 + 255) / 256) * (192 + 128) : INT64_MAX;
         if (c192 < c256) {
-            ring128_kernel<192, 128><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
+            ring128_kernel<192, 128, kExact><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
             return check_launch("gemm (192 x 128)");
         }
-        tile256_kernel<256, 128><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
+        tile256_kernel<256, 128, kExact><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 128)");
     }
     if (m <= 640 && offsets_fit) {   // too few ring tiles to fill the chip
@@ -873,25 +916,35 @@ nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* 
         if (S > 1 && part && part_bytes >= gemm_part_bytes(m, n, k) && (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
             g.ksplit = S;
             g.part = part;
-            ring128_kernel<192, 128><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
+            ring128_kernel<192, 128, kExact><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
             nhm_status s = check_launch("gemm (192 x 128, split k)");
             if (s != NHM_OK) return s;
             splitk_reduce_kernel<<<dim3((unsigned)((m * n + 1023) / 1024)), dim3(256), 0, st>>>(g);
             return check_launch("gemm split-k reduce");
         }
-        launch_panel<64, 32>(g, st);
+        launch_panel<64, 32, kExact>(g, st);
         return check_launch("gemm (panel)");
     }
     const int64_t wide_tiles = ((n + kWT - 1) / kWT) * ((m + kWT - 1) / kWT);
     if (offsets_fit && wide_tiles >= 160) {
-        tile256_kernel<256, 256><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
+        tile256_kernel<256, 256, kExact><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
         return check_launch("gemm (256 x 256)");
     }
     if (!offsets_fit)   // refused by the callers' host checks before anything is enqueued
         return fail(NHM_ERR_UNSUPPORTED, "gemm: an operand of 2 GiB or more");
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));
-    gemm_kernel<<<grid, dim3(256), 0, st>>>(g);
+    gemm_kernel<kExact><<<grid, dim3(256), 0, st>>>(g);
     return check_launch("gemm");
+}
+
+nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
+                       const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
+                       hipStream_t st, float* out_f32, float* part, size_t part_bytes, bool exact) {
+    GemmArgs g{a, lda, m, w, w_scale, a_scale, n, k, out, ld_out,
+               out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
+                       : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0,
+               out_f32};
+    return exact ? dispatch_gemm<true>(g, st, part, part_bytes) : dispatch_gemm<false>(g, st, part, part_bytes);
 }
 
 }  // namespace nhm

@@ -39,9 +39,12 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
 // partials of the shapes that take a split (m <= 640 with too few ring tiles); without it
 // those shapes run unsplit.
 size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
+// exact: every product summed in f32 (codes converted to bf16, bf16 MFMA) instead of the e4m3
+// MFMA's coarser 128-product reductions.
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st, float* out_f32 = nullptr, float* part = nullptr, size_t part_bytes = 0);
+                       hipStream_t st, float* out_f32 = nullptr, float* part = nullptr, size_t part_bytes = 0,
+                       bool exact = false);
 
 // ---- decode SSM state update (decode.hip)
 // The kernel also runs the causal conv + SiLU of the channels it reads (the head's x, the
@@ -103,7 +106,7 @@ struct PrefillArgs {
     const float* dt_bias;
     const uint16_t* norm_w;
     const float* out_a_scale;
-    uint16_t* zxbcdt;         // [T, d_in_proj] (its dt columns rewritten when exact)
+    uint16_t* zxbcdt;         // [T, d_in_proj]
     uint16_t* xbc_conv;       // [T, conv_dim]
     int32_t* chunk_info;      // [max_chunks, 4]: seq, tok0, len, index in seq
     int32_t* seq_chunk0;      // [n_seqs + 1]
@@ -113,16 +116,9 @@ struct PrefillArgs {
     uint16_t* y;              // [T, d_inner]
     uint16_t* norm;           // [T, d_inner] (nullptr: not kept)
     uint8_t* q_out;           // [T, d_inner]
-    // exact recompute of in_proj's dt columns (after the e4m3 GEMM; exact == 0: not needed)
-    int32_t exact;
-    const uint8_t* q_in;      // [T, hidden] e4m3 codes of the block input
-    const uint8_t* in_w;      // [d_in_proj, hidden] e4m3
-    const float* in_w_scale;  // [d_in_proj]
-    const float* in_a_scale;  // [1]
-    int32_t hidden;
 };
-// dt-column recompute + conv + chunk plan in one launch, then the chunked scan and the
-// gated norm + quant, in stream order.
+// conv + chunk plan in one launch, then the chunked scan and the gated norm + quant, in
+// stream order.
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st);
 
 // SSD chunk kernels on the bf16 MFMA (ssd.hip): per (chunk, head) dt, cumulative

@@ -72,69 +72,6 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ cu, int n
     }
 }
 
-// ---------------------------------------------------------------- exact dt columns
-
-// Recomputes in_proj's dt columns [dt_off, dt_off + n_heads) with exact f32 accumulation
-// (bf16 MFMA on the converted codes) after the e4m3 GEMM: dt enters the scan through
-// exp(dt * A) of every later token, where one bf16 step of dt_raw moves a long-memory
-// head's state by up to a percent, so dt gets the accumulation the reference prescribes
-// rather than the e4m3 MFMA's coarser sum. One block per 16 x 16 tile (16 tokens, 16
-// columns); its 4 waves take the 128-wide k-steps round robin with all the loads of a pass
-// in flight, and the partial tiles are summed through LDS in wave order, as in the GEMV.
-constexpr int kXWaves = 4, kXSteps = 6;   // 24 k-steps per pass: k <= 3072 in one pass
-__device__ __forceinline__ void exact_tile(const PrefillArgs& a, int64_t tile) {
-    __shared__ v4f s_red[kXWaves][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int ntc = (a.n_heads + 15) / 16;
-    const int64_t tm = tile / ntc;
-    const int tc = (int)(tile - tm * ntc);
-    const int64_t k = a.hidden;
-    const int ksteps = (int)((k + 127) / 128);
-    const int64_t t = tm * 16 + (lane & 15);                                  // B operand row (token)
-    const int64_t c0 = a.dt_off, cend = (int64_t)a.dt_off + a.n_heads;
-    const int64_t cb = c0 + (int64_t)tc * 16;
-    const int kq = (lane >> 4) * 32;
-    const __amdgpu_buffer_rsrc_t wrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.in_w, (short)0, (int)((int64_t)a.d_in_proj * k), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)a.q_in, (short)0, (int)(a.T * k), 0x00020000);
-    const uint32_t arow = t < a.T ? (uint32_t)(t * k) : kGemvOut;
-    const int64_t cw = cb + (lane & 15);                                      // A operand row (column)
-    const uint32_t wrow = cw < cend ? (uint32_t)(cw * k) : kGemvOut;
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave; s0 < ksteps; s0 += kXWaves * kXSteps) {
-        v8i xb[kXSteps], wa[kXSteps];
-#pragma unroll
-        for (int i = 0; i < kXSteps; ++i) {
-            const int s = s0 + i * kXWaves;
-            const int64_t kb = (int64_t)s * 128 + kq;
-            const bool in = s < ksteps && kb < k, in2 = s < ksteps && kb + 16 < k;
-            xb[i] = bload32<0>(ars, in ? arow + (uint32_t)kb : kGemvOut, in2 ? arow + (uint32_t)kb + 16 : kGemvOut);
-            wa[i] = bload32<0>(wrs, in ? wrow + (uint32_t)kb : kGemvOut, in2 ? wrow + (uint32_t)kb + 16 : kGemvOut);
-        }
-#pragma unroll
-        for (int i = 0; i < kXSteps; ++i) {
-            if (s0 + i * kXWaves >= ksteps) break;                        // wave-uniform
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
-                acc = mfma_bf16(e4m3x8_to_bf16(wa[i][2 * sub], wa[i][2 * sub + 1]),
-                                e4m3x8_to_bf16(xb[i][2 * sub], xb[i][2 * sub + 1]), acc);
-        }
-    }
-    if (wave > 0) s_red[wave][lane] = acc;
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 1; w < kXWaves; ++w) acc += s_red[w][lane];
-    // acc[r] = D[column cb + 4 (lane / 16) + r][token t]
-    if (t >= a.T) return;
-    const float sa = *a.in_a_scale;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t c = cb + 4 * (lane >> 4) + r;
-        if (c < cend) a.zxbcdt[t * a.d_in_proj + c] = (uint16_t)f32_to_bf16(acc[r] * (sa * a.in_w_scale[c]));
-    }
-}
-
 // ---------------------------------------------------------------- causal conv
 
 constexpr int kConvRun = 8;   // tokens per thread
@@ -157,20 +94,15 @@ __device__ __forceinline__ uint4 init_row(const PrefillArgs& a, int i, int r, in
 
 // One thread: 8 channels x kConvRun consecutive tokens. The three previous rows
 // come from the same sequence or, before its first token, from its initial window.
-// One launch for three independent jobs (none reads what another writes): blocks
-// [0, n_exact) recompute the dt columns, block n_exact computes the chunk plan, the rest
-// run the conv (channel blocks fastest).
-__global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a, int n_exact, int c8_blocks) {
+// One launch for two independent jobs (neither reads what the other writes): block 0
+// computes the chunk plan, the rest run the conv (channel blocks fastest).
+__global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a, int c8_blocks) {
     const int64_t b = blockIdx.x;
-    if (b < n_exact) {
-        exact_tile(a, b);
-        return;
-    }
-    if (b == n_exact) {
+    if (b == 0) {
         plan_block(a.cu_seqlens, a.n_seqs, a.chunk, a.max_chunks, a.chunk_info, a.seq_chunk0);
         return;
     }
-    const int64_t cbk = b - n_exact - 1;
+    const int64_t cbk = b - 1;
     const int c8 = (int)(cbk % c8_blocks) * 256 + threadIdx.x;
     if (c8 * 8 >= a.conv_dim) return;
     const int64_t t0 = (cbk / c8_blocks) * kConvRun;
@@ -304,8 +236,7 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(const PrefillArgs a) {
 nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     const int c8_blocks = (a.conv_dim / 8 + 255) / 256;
     const int64_t tblocks = (a.T + kConvRun - 1) / kConvRun;
-    const int64_t n_exact = a.exact ? ((a.T + 15) / 16) * ((a.n_heads + 15) / 16) : 0;
-    conv_fwd_kernel<<<dim3((unsigned)(n_exact + 1 + c8_blocks * tblocks)), 256, 0, st>>>(a, (int)n_exact, c8_blocks);
+    conv_fwd_kernel<<<dim3((unsigned)(1 + c8_blocks * tblocks)), 256, 0, st>>>(a, c8_blocks);
     if (a.max_chunks > 0) launch_ssd_state(a, st);
     if (a.n_seqs > 0) {
         if (a.ssm_pool_bf16)

@@ -220,6 +220,17 @@ NHM_API nhm_status nhm_fp8_linear_ex(const void* a, nhm_dtype a_type, int64_t m,
                              const nhm_fp8_weight* w, void* out, nhm_dtype out_type, int64_t ld_out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* nhm_fp8_linear_ex with every product summed in f32 on every path: the codes are converted
+ * to bf16 (exact for every e4m3 value) and summed by the bf16 MFMA, as the GEMV does for
+ * m <= 16, instead of the e4m3 MFMA's 128-product reductions. [PR988] "The Thor finding,
+ * measured": the pages' fp8 GEMM plan computes in f32 (CUBLAS_COMPUTE_32F). The result is
+ * within ~2^-24 of sum |a w| of the exact sum (measured), at up to twice the MFMA time of
+ * nhm_fp8_linear_ex for m > 16 (the bf16 MFMA runs at half the e4m3 rate). Arguments,
+ * workspace and errors are those of nhm_fp8_linear_ex. */
+NHM_API nhm_status nhm_fp8_linear_exact(const void* a, nhm_dtype a_type, int64_t m, int64_t ld_a,
+                                const nhm_fp8_weight* w, void* out, nhm_dtype out_type, int64_t ld_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- the mixer block */
 
 /* All parameters of one mixer block (device pointers; the struct itself is host).
@@ -300,9 +311,10 @@ NHM_API nhm_status nhm_mixer_prefill_ws_layout(const nhm_geometry* g, int64_t n_
  *   out         (device) bf16 [n_tokens, g.hidden]; must not overlap hidden
  *   ws          (device) >= nhm_mixer_prefill_ws_layout(g, n_tokens, n_seqs, chunk).total
  *               bytes
- * The projections follow nhm_fp8_linear (above 16 tokens the e4m3 MFMA GEMM); the
- * dt columns of in_proj, which every later token's decay exponentiates, are then
- * recomputed with exact f32 accumulation.
+ * in_proj sums every product in f32 (nhm_fp8_linear_exact): its outputs feed dt, which
+ * every later token's decay exponentiates, and the re-quantized out_proj input, whose e4m3
+ * decisions amplify one-step differences upstream. out_proj follows nhm_fp8_linear (above
+ * 16 tokens the e4m3 MFMA GEMM; its error goes to the output unamplified).
  * n_tokens == 0 with n_seqs == 0 is a valid no-op. The scan runs one block per
  * (chunk, head): (n_tokens / chunk + n_seqs) * g.n_heads above 2^31 - 1 is
  * NHM_ERR_UNSUPPORTED, and so is a projection operand of 2 GiB or more (as in

@@ -9,12 +9,9 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/nhm.h"
+#include "../../fp8_w8a8_linear_amd/csrc/nhm_internal.h"   // the launchers' declarations
 
 namespace nhm {
-struct DecodeSsmArgs;
-struct GnormArgs;
-struct PrefillArgs;
 [[noreturn]] static void reached(const char* f) {
     fprintf(stderr, "kernel launcher %s reached from a call that should have failed validation\n", f);
     abort();
@@ -33,7 +30,7 @@ nhm_status launch_gemv(const uint8_t*, int64_t, int, const uint8_t*, const float
 // they succeed, so the stub reports none.
 size_t gemm_part_bytes(int64_t, int64_t, int64_t) { return 0; }
 nhm_status launch_gemm(const uint8_t*, int64_t, int64_t, const uint8_t*, const float*, const float*, int64_t, int64_t,
-                       uint16_t*, int64_t, hipStream_t, float*, float*, size_t) {
+                       uint16_t*, int64_t, hipStream_t, float*, float*, size_t, bool) {
     reached("launch_gemm");
 }
 nhm_status launch_decode_ssm(const DecodeSsmArgs&, int, hipStream_t) { reached("launch_decode_ssm"); }

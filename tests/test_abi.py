@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(nhm):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(nhm.lib, n), f"{n} not exported"
 

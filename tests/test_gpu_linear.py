@@ -241,3 +241,37 @@ def test_linear_zero_rows(nhm):
     a = torch.empty((0, 128), dtype=torch.int16, device="cuda")
     out = nhm.fp8_linear(a, W)
     assert out.shape == (0, 64)
+
+
+# nhm_fp8_linear_exact: every product summed in f32 on every dispatch path -- the GEMV (8 x
+# 10304), the 64 x 128 panel (17 x 130, 200 x 10304), the 192 x 128 ring (384 x 10300 x 2608,
+# 512 x 10304), the 256 x 128 ring (600 x 10304), the split-k ring with its reduction (64 x
+# 4096 x 4096, 33 x 1002), the 128 x 128 tile (700 x 520 x 272) and the 256 x 256 tile (1030 x
+# 10304, 2600 x 4100 x 272). Bound: one f32 rounding of the result and of each partial sum
+# combined, |gpu - ref| <= 2^-22 |ref| + 2^-22 S (the e4m3 MFMA path needs 2^-16 S); the
+# bf16 output is the f32 result rounded once (half a bf16 step, at most 2^-8 |ref|),
+# |gpu - ref| <= 2^-8 |ref| + 2^-22 S.
+@pytest.mark.parametrize("m,n,k", [(8, 10304, 2688), (17, 130, 256), (200, 10304, 2688), (384, 10300, 2608),
+                                   (512, 10304, 2688), (600, 10304, 2688), (64, 4096, 4096), (33, 1002, 4096),
+                                   (700, 520, 272), (1030, 10304, 2688), (2600, 4100, 272)])
+def test_linear_exact(nhm, m, n, k):
+    from oracle import bf16_to_f64, e4m3_decode, fp8_linear, quantize_static
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=12)
+    q = quantize_static(a, sa)
+    ref = fp8_linear(q, w, ws, sa)
+    S = np.abs(e4m3_decode(q)) @ np.abs(e4m3_decode(w)).T * np.float64(sa[0]) * ws.astype(np.float64)[None, :]
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    ad = dev(a)
+    of = nhm.fp8_linear(ad, W, out_type=nhm.NHM_F32, exact=True)
+    ob = nhm.fp8_linear(ad, W, exact=True)
+    torch.cuda.synchronize()
+    for got, rel in ((of.cpu().numpy().astype(np.float64), 2.0 ** -22), (bf16_to_f64(host(ob)), 2.0 ** -8)):
+        err = np.abs(got - ref)
+        bound = rel * np.abs(ref) + 2.0 ** -22 * S
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert np.all(err <= bound), f"at {worst}: got {got[worst]} ref {ref[worst]} bound {bound[worst]}"
+    # the bf16 output is the f32 output rounded once
+    assert np.array_equal(of.to(torch.bfloat16).view(torch.int16).cpu().numpy(), host(ob).view(np.int16))
+    print(f"exact {m}x{n}x{k}: max |d| / (2^-24 S) = {np.max(np.abs(of.cpu().numpy() - ref) / (2.0 ** -24 * S)):.3f}")

@@ -1,11 +1,14 @@
 """Block parity: nhm_mixer_decode / nhm_mixer_prefill against the oracle.
 
-Bars (tests/gpu_util.block_parity): e4m3 bytes bit-exact (a1 on identical input;
-a9 on the GPU's own bf16 norm output); block output max|d| <= 2e-2 * RMS of the
-oracle's out_proj on the same codes; gated norm output max|d| <= 2e-2 * RMS;
-a9 codes that differ from the oracle's are adjacent and rare; f32 state
-||d||/||ref|| <= 1e-3; conv windows (bf16 copies) likewise; untouched pool rows
-bit-identical. Element counts are asserted against the geometry.
+Bars (oracle/parity.block_parity): e4m3 bytes bit-exact (a1 on identical input; a9 on the
+GPU's own bf16 norm output); the stated block tolerance max|d| <= 2e-2 * RMS end to end on
+every call of fewer than 128 tokens, and from 128 tokens on every row whose a9 codes equal
+the oracle's (the float32 floor of tests/test_oracle_noise_floor.py misses the whole-call
+bar there), with every row also held to it against the oracle's out_proj of the GPU's own
+codes; the gated norm output elementwise within its derived bound (no element exempt); a9
+codes that differ from the oracle's reachable and rare; f32 state ||d||/||ref|| <= 1e-3;
+conv windows (bf16 copies) likewise; untouched pool rows bit-identical. Element counts are
+asserted against the geometry.
 """
 import numpy as np
 import pytest
@@ -273,20 +276,20 @@ def test_mixed_batch_decode_rows_and_prefill_chunks(nhm, block0):
     touched = set(int(s) for s in sl)
     st = _check_states(spg, spr, sp, touched)
     _check_windows(cpg, cpr, cp, touched)
-    # the decode rows through the decode entry point: the projections differ in accumulation
-    # (exact f32 GEMV there, the e4m3 MFMA GEMM here at 478 tokens), so two GPU outputs are
-    # compared end to end with the bound block_parity holds that difference to (a few a9 codes
-    # flip between the paths, each moving every output), and the states and windows with the
-    # stated tolerances rather than bit equality
+    # the decode rows through the decode entry point (GEMV projections, the per-token state
+    # update) and through this prefill call (tiled GEMMs, the chunked scan) differ in float
+    # rounding only: both are checked against the oracle, and their states and windows against
+    # each other with the stated tolerances rather than bit equality
     dec = [i for i, L in enumerate(lens) if L == 1]
     rows = cu[dec]
-    od, spd, cpd, _, _ = _gpu_decode(nhm, pd, h[rows], sl[dec], sp, cp)
-    assert rel_max(bf16_to_f64(od), bf16_to_f64(out[rows])) <= 0.1
+    od, spd, cpd, wsd, layd = _gpu_decode(nhm, pd, h[rows], sl[dec], sp, cp)
+    # the decode rows through nhm_mixer_decode against the oracle's results for the same rows
+    md = _parity(od, wsd, layd, list(range(len(dec))), ref[rows], norm[rows], q[rows], block0)
     for s in sl[dec]:
         assert rel_l2(spd[s], spg[s]) <= TOL_STATE
         a, b = bf16_to_f64(cpd[s]), bf16_to_f64(cpg[s])
         assert rel_l2(a, b) <= TOL_STATE and rel_max(a, b) <= TOL_OUT
-    print(f"mixed batch {lens}: {m}, state rel l2 {st:.3e}")
+    print(f"mixed batch {lens}: {m}, state rel l2 {st:.3e}; its decode rows through nhm_mixer_decode: {md}")
 
 
 def _check_states_bf16(sp_gpu, sp_ref, sp_before, touched):
