@@ -13,7 +13,7 @@ import os
 __all__ = ["lib", "LIB_PATH", "NhmError", "Geometry", "Layout", "WsLayout", "Fp8Weight", "MixerParams",
            "GEOMETRY", "mixer_layout", "quantize_static", "fp8_linear", "fp8_linear_workspace_bytes",
            "decode_ws_layout", "prefill_ws_layout", "mixer_decode", "mixer_prefill", "NHM_BF16", "NHM_E4M3",
-           "NHM_F32", "fp8_dequant_channel_bf16"]
+           "NHM_F32", "fp8_dequant_channel_bf16", "mixer_decode_noalloc"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnhm.so")
 if not os.path.exists(LIB_PATH):
@@ -78,6 +78,7 @@ _SIGS = {
                                     _p, _sz, _p]),
     "nhm_mixer_decode_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p, _sz,
                                       _p]),
+    "nhm_mixer_decode_noalloc": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p]),
     "nhm_mixer_prefill_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i64, _p, _i32, _p, _p, _i32, _p, C.c_int, _p,
                                        _i32, _p, _p, _sz, _p]),
 }
@@ -237,6 +238,16 @@ def mixer_decode(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out
     _check(lib.nhm_mixer_decode_ex(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
                                    _ssm_type(ssm_pool), _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws),
                                    ws.numel(), _stream(stream)))
+    return out
+
+
+def mixer_decode_noalloc(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out, stream=None):
+    """mixer_decode with the library's per-device scratch instead of a workspace (nothing is
+    allocated by the call; calls that overlap on one GPU race)."""
+    batch = int(hidden.shape[0])
+    _check(lib.nhm_mixer_decode_noalloc(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
+                                        _ssm_type(ssm_pool), _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out),
+                                        _stream(stream)))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "nhm_device.h"
 #include "nhm_internal.h"
@@ -348,9 +349,57 @@ nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* hidden, i
                                stream);
 }
 
-nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
-                               const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
-                               int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace nhm {
+
+// ---------------------------------------------------------------- decode scratch without allocation
+// nhm_mixer_decode_noalloc keeps its workspace in this file-scope device array instead of a
+// caller's buffer. Each GPU the library runs on holds its own copy, at its own address, until
+// the process ends; host code reaches it only through the address hipGetSymbolAddress returns
+// on that device (the array's name is a host-side stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// The scratch address on the device the call's work runs on: resolved once per device, on
+// that device's first call (the current device, which must be the stream's).
+static nhm_status device_scratch(hipStream_t st, void** out) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NHM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    if (st) {
+        int sd = -1;
+        e = hipStreamGetDevice(st, &sd);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NHM_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        }
+        if (sd != cur)
+            return fail(NHM_ERR_UNSUPPORTED, "the stream belongs to device %d but device %d is current", sd, cur);
+    }
+    if (cur < 0 || cur >= kMaxDevices) return fail(NHM_ERR_UNSUPPORTED, "device %d: at most %d devices", cur, kMaxDevices);
+    void* p = g_scratch_addr[cur].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(NHM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", cur, hipGetErrorString(e));
+        }
+        g_scratch_addr[cur].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return NHM_OK;
+}
+
+// nhm_mixer_decode_ex; noalloc: the workspace is this library's device scratch (ws ignored).
+static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                              const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
+                              int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream, bool noalloc) {
     g_err[0] = 0;
     if (ssm_type != NHM_F32 && ssm_type != NHM_BF16)
         return fail(NHM_ERR_UNSUPPORTED, "SSM state dtype %d: f32 or bf16", (int)ssm_type);
@@ -360,18 +409,22 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
     if (batch < 0) return fail(NHM_ERR_SHAPE, "negative batch");
     if (batch == 0) return NHM_OK;
     if (n_slots <= 0) return fail(NHM_ERR_SHAPE, "n_slots must be positive");
-    if (!hidden || !slot_idx || !ssm_pool || !conv_pool || !out || !ws)
+    if (!hidden || !slot_idx || !ssm_pool || !conv_pool || !out || (!noalloc && !ws))
         return fail(NHM_ERR_NULL, "hidden, slot_idx, pools, out or ws is NULL");
     if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
-        !aligned(slot_idx, 4) || !aligned(ws, 256))
+        !aligned(slot_idx, 4) || (!noalloc && !aligned(ws, 256)))
         return fail(NHM_ERR_ALIGN, "hidden, out and pools must be 16-byte aligned, ws 256-byte aligned");
     const MixerWs w = decode_ws(&p->g, batch);
-    if (ws_bytes < w.pub.total)
+    if (noalloc && w.pub.total > kNoAllocScratchBytes)
+        return fail(NHM_ERR_WORKSPACE, "batch %d needs %zu bytes of scratch; the library's per-device scratch holds %zu",
+                    batch, w.pub.total, kNoAllocScratchBytes);
+    if (!noalloc && ws_bytes < w.pub.total)
         return fail(NHM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.pub.total, ws_bytes);
     if ((s = check_offsets(batch, p->g.hidden, l.d_in_proj, p->g.hidden, "decode in_proj")) != NHM_OK ||
         (s = check_offsets(batch, l.d_inner, p->g.hidden, l.d_inner, "decode out_proj")) != NHM_OK)
         return s;
     hipStream_t st = (hipStream_t)stream;
+    if (noalloc && (s = device_scratch(st, &ws)) != NHM_OK) return s;
     char* wsb = static_cast<char*>(ws);
     const int64_t H = p->g.hidden;
     uint8_t* q_in = reinterpret_cast<uint8_t*>(wsb + w.pub.q_in);
@@ -433,6 +486,24 @@ nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden
         if (s != NHM_OK) return s;
     }
     return NHM_OK;
+}
+
+}  // namespace nhm
+
+extern "C" {
+
+nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                               const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
+                               int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    return decode_call(p, hidden, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, ws, ws_bytes, stream,
+                       false);
+}
+
+nhm_status nhm_mixer_decode_noalloc(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                                    const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
+                                    int32_t n_slots, uint16_t* out, void* stream) {
+    return decode_call(p, hidden, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, nullptr, 0, stream,
+                       true);
 }
 
 nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,

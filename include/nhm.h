@@ -288,6 +288,22 @@ NHM_API nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* h
                             int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* nhm_mixer_decode_ex without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The intermediates go to a scratch array that the library holds in device memory, 16 MiB per
+ * GPU it runs on, kept until the process ends; the call itself allocates nothing. A call
+ * whose workspace (nhm_mixer_decode_ws_layout(g, batch).total) exceeds 16 MiB is refused with
+ * NHM_ERR_WORKSPACE before anything is enqueued: batch <= 299 at the NemotronH geometry
+ * (16.76 MB at 299 rows). Every call on one GPU from one process shares that GPU's scratch (another
+ * process holds its own copy): calls that can overlap there (on two streams, from two
+ * threads) race and must not be issued. The scratch keeps the last call's intermediates;
+ * nothing in it needs to start at zero. The stream must belong to the current device (else NHM_ERR_UNSUPPORTED);
+ * the first call on a device resolves that device's scratch address. Every other argument,
+ * the results and the remaining errors are those of nhm_mixer_decode_ex. */
+NHM_API nhm_status nhm_mixer_decode_noalloc(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
+                                    const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type,
+                                    uint16_t* conv_pool, int32_t n_slots, uint16_t* out, void* stream);
+
 /* Workspace layout of nhm_mixer_prefill for up to n_tokens tokens in up to n_seqs
  * sequences with SSD chunk length `chunk`. total also covers scratch the layout does not
  * name: the chunk plan, per-chunk decays and states, and the projections' split-k partials.

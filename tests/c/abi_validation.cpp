@@ -130,6 +130,12 @@ int main() {
     nhm_mixer_params pw = p;
     pw.in_proj.k = 4096;
     EXPECT(nhm_mixer_decode(&pw, H, 8, SL, SP, CP, 64, O, WS, dl.total, nullptr), NHM_ERR_SHAPE);
+    // the no-allocation decode: refused before any device call (its scratch holds batch <= 299)
+    EXPECT(nhm_mixer_decode_noalloc(&p, H, 0, SL, SP, NHM_F32, CP, 64, O, nullptr), NHM_OK);
+    EXPECT(nhm_mixer_decode_noalloc(&p, H, 300, SL, SP, NHM_F32, CP, 512, O, nullptr), NHM_ERR_WORKSPACE);
+    EXPECT(nhm_mixer_decode_noalloc(&p, nullptr, 8, SL, SP, NHM_F32, CP, 64, O, nullptr), NHM_ERR_NULL);
+    EXPECT(nhm_mixer_decode_noalloc(&p, H + 4, 8, SL, SP, NHM_F32, CP, 64, O, nullptr), NHM_ERR_ALIGN);
+    EXPECT(nhm_mixer_decode_noalloc(&p, H, 8, SL, SP, (nhm_dtype)5, CP, 64, O, nullptr), NHM_ERR_UNSUPPORTED);
     nhm_ws_layout pl;
     EXPECT(nhm_mixer_prefill_ws_layout(&g, 512, 1, 128, &pl), NHM_OK);
     const int32_t* CU = (const int32_t*)P(0x700000);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(nhm):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(nhm.lib, n), f"{n} not exported"
 
@@ -184,6 +184,24 @@ def test_decode_refusals(nhm):
     p = _params(nhm)
     p.g = g
     assert call(p=p) == 4
+
+
+def test_decode_noalloc_refusals(nhm):
+    """The no-allocation decode validates like nhm_mixer_decode_ex and refuses a batch whose
+    workspace exceeds its 16 MiB per-device scratch (300 rows at this geometry), before any
+    device call."""
+    f = nhm.lib.nhm_mixer_decode_noalloc
+    H, SL, SP, CP, O = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    p = _params(nhm)
+    assert f(C.byref(p), H, 0, SL, SP, nhm.NHM_F32, CP, 64, O, None) == 0
+    assert nhm.decode_ws_layout(299)["total"] <= 16 << 20 < nhm.decode_ws_layout(300)["total"]
+    assert f(C.byref(p), H, 300, SL, SP, nhm.NHM_F32, CP, 512, O, None) == 5
+    assert b"scratch" in nhm.lib.nhm_last_error()
+    assert f(C.byref(p), None, 8, SL, SP, nhm.NHM_F32, CP, 64, O, None) == 1
+    assert f(C.byref(p), H, 8, SL, SP, nhm.NHM_F32, CP, 64, None, None) == 1
+    assert f(C.byref(p), H + 8, 8, SL, SP, nhm.NHM_F32, CP, 64, O, None) == 3
+    assert f(C.byref(p), H, 8, SL, SP, 7, CP, 64, O, None) == 4
+    assert f(C.byref(p), H, -1, SL, SP, nhm.NHM_F32, CP, 64, O, None) == 2
 
 
 def test_prefill_refusals(nhm):

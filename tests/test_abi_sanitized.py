@@ -1,4 +1,4 @@
-"""The C ABI's host validation (csrc/api.hip, compiled for the host only) under
+"""The C ABI's host validation (csrc/api.hip) under
 AddressSanitizer and UndefinedBehaviorSanitizer: tests/c/abi_validation.cpp calls every
 entry point with refused arguments and the pure host queries, and any out-of-bounds
 access, leak-free misuse or undefined behaviour in the validation aborts the run. No GPU:
@@ -22,10 +22,12 @@ def _hipcc():
 def test_abi_validation_under_asan_ubsan(tmp_path):
     hipcc = _hipcc()
     exe = str(tmp_path / "abi_validation")
-    # host-only compilation; the sanitizer flags apply to the host pass only
+    # the sanitizer flags apply to the host pass only (api.hip's device half -- its scratch
+    # array -- is compiled plainly)
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
-    cmd = [hipcc, "-std=c++17", "-O1", "-g", "--offload-host-only", "--offload-arch=gfx950", *san,
+    cmd = [hipcc, "-std=c++17", "-O1", "-g", "--offload-arch=gfx950", *san,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"),
            os.path.join(ROOT, "fp8_w8a8_linear_amd", "csrc", "api.hip"),
            os.path.join(ROOT, "tests", "c", "abi_validation.cpp"), "-o", exe]
