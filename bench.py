@@ -1,17 +1,23 @@
 #!/usr/bin/env python3
 """Mixer throughput on one MI355X: paged decode B=8 through 23 stacked blocks (the
 headline line), the same step on bf16 state pools (decode_bf16_state), prefill of one
-512-token sequence through one block, and one block of the ragged prefill (8192 + 4096 +
-2048 + 1024 tokens).
+512-token sequence through one block, one block of the ragged prefill (8192 + 4096 +
+2048 + 1024 tokens), the W8A8 projections at the prefill sizes and the six-shape linear
+sweep.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
 
-A step is one decode token for each of 8 sequences through all 23 mixer blocks
-(nhm_mixer_decode per block, state rows updated in place), replayed as one HIP
-graph. Inputs are seeded synthetic tensors already resident in HBM. After all GPU
-timing, layers 0 and 1 of one step from their seeded pools are checked against the
-oracle (block parity and the updated f32 states); that same oracle run, timed on the
-host cores, is the cpu_baseline. Prints ONE JSON line on stdout; progress goes to stderr.
+A step is one decode token for each of 8 sequences through all 23 mixer blocks, replayed
+as one HIP graph: block 0 quantizes its bf16 input, and every block's out_proj also writes
+the codes of its output under the next block's input scale, which the next block takes as
+its pre-quantized input (nhm_mixer_decode_q); state rows are updated in place. Inputs are
+seeded synthetic tensors already resident in HBM. Every timed figure is the median of at
+least five repeats (the headline times exactly K steps, in five consecutive groups whose
+median is reported beside it). The library's dispatch counters of one eager decode step and
+one prefill call are printed and checked as path-taken evidence. After all GPU timing,
+layers 0 and 1 of one step from their seeded pools are checked against the oracle (block
+parity and the updated f32 states); that same oracle run, timed on the host, is the
+cpu_baseline. Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
@@ -24,12 +30,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-N_LAYERS, BATCH, SLOTS, HIDDEN, INNER = 23, 8, 64, 2688, 4096
+N_LAYERS, BATCH, SLOTS, HIDDEN, INNER, D_IN_PROJ = 23, 8, 64, 2688, 4096, 10304
 HBM_PEAK_GBS = 8000.0
-FP8_PEAK_TFLOPS = 5000.0
+FP8_PEAK_TFLOPS = 5000.0          # dense e4m3 MFMA
+BF16_PEAK_TFLOPS = 2500.0         # dense bf16 MFMA (the exact-sum GEMMs run on it)
 WORKLOAD_DECODE = 2          # paged decode B=8, 23 blocks
 WORKLOAD_PREFILL = 3         # prefill 512, one block
 WORKLOAD_RAGGED = 4          # ragged prefill 8192 + 4096 + 2048 + 1024 tokens, zero initial state
+REPEATS = 5
 
 
 def log(msg):
@@ -70,6 +78,24 @@ def gemv_bytes(m, n, k):
     return n * k + 4 * n + m * k + 2 * m * n
 
 
+def host_cpu():
+    """(logical CPUs of the host, CPUs this process may run on, CPU model)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return os.cpu_count(), affinity, model
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,7 +115,7 @@ def main():
 
     import torch
     import fp8_w8a8_linear_amd as nhm
-    from workloads import block_params, conv_pool, hidden, slots, ssm_pool
+    from workloads import LINEAR_SHAPES, RAGGED_LENGTHS, bf16_bits, block_params, conv_pool, hidden, slots, ssm_pool
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -109,6 +135,42 @@ def main():
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
+    def upload(p):
+        return nhm.MixerParams(nhm.Fp8Weight(up(p["in_w"]), up(p["in_w_scale"]), up(p["in_a_scale"])),
+                               nhm.Fp8Weight(up(p["out_w"]), up(p["out_w_scale"]), up(p["out_a_scale"])),
+                               up(p["conv_w"]), up(p["conv_b"]), up(p["norm_w"]), up(p["A_log"]), up(p["D"]),
+                               up(p["dt_bias"]))
+
+    cap = torch.cuda.Stream()   # graphs are captured on this stream and replayed on the current one
+
+    def time_repeats(fn, iters, repeats=REPEATS):
+        """Median and all repeats of the per-iteration time (us) of fn(), each repeat timed with
+        HIP events on the current stream, where fn's work runs (eager calls and graph replays)."""
+        st = torch.cuda.current_stream()
+        out = []
+        for _ in range(repeats):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for _ in range(iters):
+                fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / iters)
+        if not min(out) > 0:
+            print("refusing to report a rate over a non-positive window", file=sys.stderr)
+            sys.exit(3)
+        return float(np.median(out)), [round(x, 2) for x in out]
+
+    def graph_of(fn):
+        with torch.cuda.stream(cap):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
     # ------------------------------------------------------------ decode inputs
     t0 = time.time()
     params, host_params, spools, cpools, host_pools = [], [], [], [], {}
@@ -118,10 +180,7 @@ def main():
         if layer < 2:
             host_params.append(p)
             host_pools[layer] = (sp, cp)
-        params.append(nhm.MixerParams(nhm.Fp8Weight(up(p["in_w"]), up(p["in_w_scale"]), up(p["in_a_scale"])),
-                                      nhm.Fp8Weight(up(p["out_w"]), up(p["out_w_scale"]), up(p["out_a_scale"])),
-                                      up(p["conv_w"]), up(p["conv_b"]), up(p["norm_w"]), up(p["A_log"]),
-                                      up(p["D"]), up(p["dt_bias"])))
+        params.append(upload(p))
         spools.append(up(sp))
         cpools.append(up(cp))
         if layer % 6 == 5:
@@ -133,111 +192,98 @@ def main():
     lay = nhm.decode_ws_layout(BATCH)
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device=dev)
     acts = [x0] + [torch.empty((BATCH, HIDDEN), dtype=torch.int16, device=dev) for _ in range(N_LAYERS)]
+    codes = [None] + [torch.empty((BATCH, HIDDEN), dtype=torch.uint8, device=dev) for _ in range(N_LAYERS - 1)]
     torch.cuda.synchronize()
     log(f"decode inputs resident ({time.time() - t0:.0f} s)")
 
-    def step(stream=None):
+    def step(pools=None, stream=None):
+        """One decode step: block 0 quantizes its bf16 input; each block's out_proj also emits the
+        next block's input codes (under that block's in_proj scale)."""
+        pools = pools or spools
         for l in range(N_LAYERS):
-            nhm.mixer_decode(params[l], acts[l], sl, spools[l], cpools[l], acts[l + 1], ws, stream=stream)
+            nxt = params[l + 1].in_proj.a_scale if l + 1 < N_LAYERS else None
+            nhm.mixer_decode_q(params[l], acts[l] if l == 0 else None, sl, pools[l], cpools[l], acts[l + 1], ws,
+                               hidden_q=codes[l], out_q=codes[l + 1] if l + 1 < N_LAYERS else None,
+                               out_q_scale=nxt, stream=stream)
 
-    # ------------------------------------------------------------ graph capture and timing
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        step()
-    torch.cuda.current_stream().wait_stream(cap)
+    # path-taken evidence: the kernels one eager step launches
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        step()
+    nhm.dispatch_counters(reset=True)
+    step()
     torch.cuda.synchronize()
+    decode_path = nhm.dispatch_counters(reset=True)
+    want = {"quant_vec8": (1, BATCH), "gemv": (2 * N_LAYERS, 2 * N_LAYERS * BATCH),
+            "decode_ssm": (N_LAYERS, N_LAYERS * BATCH), "gnorm_quant": (N_LAYERS, N_LAYERS * BATCH)}
+    assert decode_path == want, f"decode step dispatched {decode_path}, expected {want}"
+    log(f"decode step path: {decode_path}")
+
+    # ------------------------------------------------------------ headline: K graph-replayed steps
+    graph = graph_of(step)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record()
+    groups = REPEATS if args.steps >= REPEATS else 1
+    sizes = [args.steps // groups + (1 if i < args.steps % groups else 0) for i in range(groups)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    evs[0].record()
+    for gi, n in enumerate(sizes):
+        for _ in range(n):
+            graph.replay()
+        evs[gi + 1].record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms_step = total_ms / args.steps
     if not ms_step > 0:
         print("refusing to report a rate over a non-positive window", file=sys.stderr)
         sys.exit(3)
+    group_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / sizes[i] for i in range(groups)]
     tok_s = BATCH / (ms_step * 1e-3)
     step_bytes = N_LAYERS * decode_bytes_per_layer(BATCH)
-    log(f"decode step {ms_step * 1e3:.1f} us, {tok_s:.0f} tokens/s, step HBM {step_bytes / ms_step / 1e6:.0f} GB/s")
+    log(f"decode step {ms_step * 1e3:.1f} us (groups {[round(u, 1) for u in group_us]}), {tok_s:.0f} tokens/s, "
+        f"step HBM {step_bytes / ms_step / 1e6:.0f} GB/s")
 
     # ------------------------------------------------------------ dominant kernel: in_proj GEMV, m=8
-    s = torch.cuda.current_stream()
-    qin = ws[lay["q_in"]:lay["q_in"] + BATCH * HIDDEN].view(BATCH, HIDDEN)
-    gout = torch.empty((BATCH, 10304), dtype=torch.int16, device=dev)
-    gws = torch.zeros(max(nhm.fp8_linear_workspace_bytes(BATCH, 10304, HIDDEN, nhm.NHM_E4M3), 256),
+    qin = codes[1]   # block 1's input codes, as the step feeds them
+    gout = torch.empty((BATCH, D_IN_PROJ), dtype=torch.int16, device=dev)
+    gws = torch.zeros(max(nhm.fp8_linear_workspace_bytes(BATCH, D_IN_PROJ, HIDDEN, nhm.NHM_E4M3), 256),
                       dtype=torch.uint8, device=dev)
-    # one launch per layer's weights (890 MB cycle, far above the 256 MB MALL), captured as a
-    # graph so the host's launch rate does not pace a ~10 us kernel
-    for l in range(N_LAYERS):
-        nhm.fp8_linear(qin, params[l].in_proj, out=gout, ws=gws, a_type=nhm.NHM_E4M3)
-    torch.cuda.synchronize()
-    rg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(rg, stream=cap):
+
+    def gemv_pass():   # one launch per layer's weights (890 MB cycle, far above the 256 MB MALL)
         for l in range(N_LAYERS):
             nhm.fp8_linear(qin, params[l].in_proj, out=gout, ws=gws, a_type=nhm.NHM_E4M3)
+
+    rg = graph_of(gemv_pass)   # captured, so the host's launch rate does not pace a ~10 us kernel
     for _ in range(3):
         rg.replay()
     torch.cuda.synchronize()
-    passes = 20
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(s)
-    for _ in range(passes):
-        rg.replay()
-    g1.record(s)
-    torch.cuda.synchronize()
-    gemv_us = g0.elapsed_time(g1) * 1e3 / (passes * N_LAYERS)
-    gb = gemv_bytes(BATCH, 10304, HIDDEN)
+    pass_us, pass_all = time_repeats(rg.replay, 4)
+    gemv_us = pass_us / N_LAYERS
+    gb = gemv_bytes(BATCH, D_IN_PROJ, HIDDEN)
     achieved = gb / (gemv_us * 1e-6) / 1e9
-    log(f"in_proj GEMV m=8: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s")
+    log(f"in_proj GEMV m=8: {gemv_us:.2f} us/launch (median of {REPEATS}: "
+        f"{[round(u / N_LAYERS, 2) for u in pass_all]}), {achieved:.0f} GB/s")
+    del rg
 
     # ------------------------------------------------------------ decode with a bf16 state pool
     # the same step on bf16 copies of the state pools (rows widened to f32 in the kernel and
     # rounded back on store): half the state bytes
     spools16 = [sp.to(torch.bfloat16).view(torch.int16) for sp in spools]
     torch.cuda.synchronize()
-
-    def step16(stream=None):
-        for l in range(N_LAYERS):
-            nhm.mixer_decode(params[l], acts[l], sl, spools16[l], cpools[l], acts[l + 1], ws, stream=stream)
-
-    with torch.cuda.stream(cap):
-        step16()
-    torch.cuda.current_stream().wait_stream(cap)
-    torch.cuda.synchronize()
-    graph16 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph16, stream=cap):
-        step16()
-    torch.cuda.synchronize()
+    graph16 = graph_of(lambda: step(spools16))
     for _ in range(args.warmup):
         graph16.replay()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        graph16.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms16 = e0.elapsed_time(e1) / args.steps
+    us16, all16 = time_repeats(graph16.replay, max(args.steps // REPEATS, 1))
     bytes16 = N_LAYERS * decode_bytes_per_layer(BATCH, state_bytes=2)
-    dec16 = {"us_per_step": round(ms16 * 1e3, 1), "tokens_per_s": round(BATCH / (ms16 * 1e-3), 1), "bytes": bytes16,
-             "achieved_GBs": round(bytes16 / (ms16 * 1e-3) / 1e9, 1),
-             "frac": round(bytes16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    dec16 = {"us_per_step": round(us16, 1), "repeats_us": all16, "tokens_per_s": round(BATCH / (us16 * 1e-6), 1),
+             "bytes": bytes16, "achieved_GBs": round(bytes16 / (us16 * 1e-6) / 1e9, 1),
+             "frac": round(bytes16 / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"decode step, bf16 state pools: {dec16}")
-    del spools16, graph16
+    del spools16, graph16, graph
 
     # ------------------------------------------------------------ prefill 512, one block
     pp = block_params(WORKLOAD_PREFILL, 0)
-    ppar = nhm.MixerParams(nhm.Fp8Weight(up(pp["in_w"]), up(pp["in_w_scale"]), up(pp["in_a_scale"])),
-                           nhm.Fp8Weight(up(pp["out_w"]), up(pp["out_w_scale"]), up(pp["out_a_scale"])),
-                           up(pp["conv_w"]), up(pp["conv_b"]), up(pp["norm_w"]), up(pp["A_log"]), up(pp["D"]),
-                           up(pp["dt_bias"]))
+    ppar = upload(pp)
     T = 512
     ph = up(hidden(WORKLOAD_PREFILL, T))
     psp, pcp = up(ssm_pool(WORKLOAD_PREFILL, 0, 2)), up(conv_pool(WORKLOAD_PREFILL, 0, 2))
@@ -248,76 +294,79 @@ def main():
     def pstep():
         nhm.mixer_prefill(ppar, ph, pcu, psl, phi, psp, pcp, pout, pws)
 
-    pg = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        pstep()
+    nhm.dispatch_counters(reset=True)
+    pstep()
     torch.cuda.synchronize()
-    with torch.cuda.graph(pg, stream=cap):
-        pstep()
+    prefill_path = nhm.dispatch_counters(reset=True)
+    for k_ in ("quant_vec8", "gemm_ring192x128_exact", "conv_fwd", "ssd_state", "ssd_pass", "ssd_out", "gnorm_quant"):
+        assert k_ in prefill_path, f"prefill 512 did not launch {k_}: {prefill_path}"
+    assert not any(k_.startswith("gemv") for k_ in prefill_path), prefill_path
+    log(f"prefill 512 path: {prefill_path}")
+    pg = graph_of(pstep)
     for _ in range(5):
         pg.replay()
     torch.cuda.synchronize()
-    preps = 50
-    e0.record()
-    for _ in range(preps):
-        pg.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    pre_us = e0.elapsed_time(e1) * 1e3 / preps
-    # the two fp8 GEMMs of that block, alone, on the codes the block feeds them: bf16 ~ N(0,1)
-    # activations (the block input; the gated norm's output is of the same scale) quantized by
-    # the library with the projection's static scale
-    from workloads import bf16_bits
+    pre_us, pre_all = time_repeats(pg.replay, 20)
+    del pg
 
+    # the projections of that block, alone, on the codes the block feeds them (bf16 ~ N(0,1)
+    # activations quantized by the library with the projection's static scale): in_proj with
+    # every product summed in f32, as the block runs it (bf16 MFMA), and both projections on the
+    # e4m3 MFMA (nhm_fp8_linear)
     def act_codes(rows, k, w, seed):
         x = up(bf16_bits(np.random.default_rng(seed).standard_normal((rows, k), dtype=np.float32)))
         q = nhm.quantize_static(x, w.a_scale)
         torch.cuda.synchronize()
         return q
 
-    gemm = {}
-    for name, (n, k) in {"in_proj": (10304, 2688), "out_proj": (2688, 4096)}.items():
-        w = ppar.in_proj if name == "in_proj" else ppar.out_proj
-        a = act_codes(T, k, w, 7001 + k)
-        o = torch.empty((T, n), dtype=torch.int16, device=dev)
+    def time_linear(m, w, seed, exact, iters):
+        a = act_codes(m, w.k, w, seed)
+        o = torch.empty((m, w.n), dtype=torch.int16, device=dev)
+        wsl = torch.zeros(max(nhm.fp8_linear_workspace_bytes(m, w.n, w.k, nhm.NHM_E4M3), 256), dtype=torch.uint8,
+                          device=dev)
+        f = lambda: nhm.fp8_linear(a, w, out=o, ws=wsl, a_type=nhm.NHM_E4M3, exact=exact)  # noqa: E731
         for _ in range(3):
-            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
+            f()
         torch.cuda.synchronize()
-        g0.record(s)
-        for _ in range(50):
-            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
-        g1.record(s)
-        torch.cuda.synchronize()
-        us = g0.elapsed_time(g1) * 1e3 / 50
-        gemm[name] = {"us": round(us, 2), "tflops": round(2 * T * n * k / (us * 1e-6) / 1e12, 1)}
-    # the same two projections at the ragged-prefill size (15,360 tokens), where the GEMM has
-    # enough arithmetic per weight byte to be bound by the MFMA rather than by operand delivery
+        us, all_ = time_repeats(f, iters)
+        tf = 2 * m * w.n * w.k / (us * 1e-6) / 1e12
+        peak = BF16_PEAK_TFLOPS if exact else FP8_PEAK_TFLOPS
+        return {"us": round(us, 2), "repeats_us": all_, "tflops": round(tf, 1),
+                "mfma": "bf16 (codes converted exactly, f32 sums)" if exact else "e4m3",
+                "frac_peak": round(tf / peak, 4)}
+
+    gemm = {"in_proj": time_linear(T, ppar.in_proj, 7001 + HIDDEN, True, 50),
+            "out_proj": time_linear(T, ppar.out_proj, 7001 + INNER, False, 50),
+            "in_proj_e4m3": time_linear(T, ppar.in_proj, 7001 + HIDDEN, False, 50)}
+    blk_gemm_us = gemm["in_proj"]["us"] + gemm["out_proj"]["us"]
+    log(f"prefill 512: {pre_us:.1f} us/block {pre_all}, {T / (pre_us * 1e-6):.0f} tokens/s; GEMMs {gemm}")
+    # the same at the ragged-prefill size (15,360 tokens), where the GEMMs have enough arithmetic
+    # per weight byte to be bound by the MFMA rather than by operand delivery
     TL = 15360
-    gemm_large = {}
-    for name, (n, k) in {"in_proj": (10304, 2688), "out_proj": (2688, 4096)}.items():
-        w = ppar.in_proj if name == "in_proj" else ppar.out_proj
-        a = act_codes(TL, k, w, 7101 + k)
-        o = torch.empty((TL, n), dtype=torch.int16, device=dev)
-        for _ in range(2):
-            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
-        torch.cuda.synchronize()
-        g0.record(s)
-        for _ in range(10):
-            nhm.fp8_linear(a, w, out=o, a_type=nhm.NHM_E4M3)
-        g1.record(s)
-        torch.cuda.synchronize()
-        us = g0.elapsed_time(g1) * 1e3 / 10
-        tf = 2 * TL * n * k / (us * 1e-6) / 1e12
-        gemm_large[name] = {"us": round(us, 1), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
-        del a, o
-    log(f"GEMMs at m = {TL}: {gemm_large}")
-    # one block of the ragged prefill (4 sequences, 15,360 tokens, zero initial state), replayed
-    from workloads import RAGGED_LENGTHS
+    gemm_large = {"in_proj": time_linear(TL, ppar.in_proj, 7101 + HIDDEN, True, 3),
+                  "out_proj": time_linear(TL, ppar.out_proj, 7101 + INNER, False, 3),
+                  "in_proj_e4m3": time_linear(TL, ppar.in_proj, 7101 + HIDDEN, False, 3)}
+    log(f"projections at m = {TL}: {gemm_large}")
+
+    # ------------------------------------------------------------ the six-shape W8A8 linear sweep
+    sweep = {}
+    for (m, n, k) in LINEAR_SHAPES:
+        w = ppar.in_proj if (n, k) == (D_IN_PROJ, HIDDEN) else ppar.out_proj if (n, k) == (HIDDEN, INNER) else None
+        if w is None:   # the square control
+            from workloads import linear_case
+            _, wq, wsc, sa = linear_case(m, n, k)
+            w = nhm.Fp8Weight(up(wq), up(wsc), up(sa))
+        r = time_linear(m, w, 7201 + m + n, False, 50 if m < 4096 else 5)
+        byts = gemv_bytes(m, n, k)
+        r["GBs"] = round(byts / (r["us"] * 1e-6) / 1e9, 1)
+        r["frac_hbm"] = round(r["GBs"] / HBM_PEAK_GBS, 4)
+        r["bound"] = "hbm" if 2 * m * n * k / byts < 5e15 / 8e12 else "mfma"
+        sweep[f"{m}x{n}x{k}"] = r
+    log(f"linear sweep: { {s: (v['us'], v['bound']) for s, v in sweep.items()} }")
+
+    # ------------------------------------------------------------ one block of the ragged prefill
     rp = block_params(WORKLOAD_RAGGED, 0)
-    rpar = nhm.MixerParams(nhm.Fp8Weight(up(rp["in_w"]), up(rp["in_w_scale"]), up(rp["in_a_scale"])),
-                           nhm.Fp8Weight(up(rp["out_w"]), up(rp["out_w_scale"]), up(rp["out_a_scale"])),
-                           up(rp["conv_w"]), up(rp["conv_b"]), up(rp["norm_w"]), up(rp["A_log"]), up(rp["D"]),
-                           up(rp["dt_bias"]))
+    rpar = upload(rp)
     rl = list(RAGGED_LENGTHS)
     RT = int(sum(rl))
     rh = up(hidden(WORKLOAD_RAGGED, RT))
@@ -328,26 +377,13 @@ def main():
     rhi = up(np.zeros(len(rl), np.int32))
     rws = torch.zeros(nhm.prefill_ws_layout(RT, len(rl))["total"], dtype=torch.uint8, device=dev)
     rout = torch.empty((RT, HIDDEN), dtype=torch.int16, device=dev)
-    rg = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(rg, stream=cap):
-        nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws)
+    rgr = graph_of(lambda: nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws))
     for _ in range(2):
-        rg.replay()
+        rgr.replay()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        rg.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    rag_us = e0.elapsed_time(e1) * 1e3 / 10
-    log(f"ragged prefill {rl}: {rag_us:.1f} us/block, {RT / (rag_us * 1e-6):.0f} tokens/s")
-    del rh, rws, rout, rsp, rcp
-    gemm_us = gemm["in_proj"]["us"] + gemm["out_proj"]["us"]
-    gemm_tflops = 2 * T * 38707200 / (gemm_us * 1e-6) / 1e12
-    log(f"prefill 512: {pre_us:.1f} us/block, {T / (pre_us * 1e-6):.0f} tokens/s; GEMMs {gemm}")
+    rag_us, rag_all = time_repeats(rgr.replay, 2)
+    log(f"ragged prefill {rl}: {rag_us:.1f} us/block {rag_all}, {RT / (rag_us * 1e-6):.0f} tokens/s")
+    del rh, rws, rout, rsp, rcp, rgr
 
     # ------------------------------------------------------------ parity sample + cpu baseline
     # after every GPU measurement (the oracle's host threads cannot disturb them); layers 0-1
@@ -385,12 +421,15 @@ def main():
             parity[f"layer{layer}"] = entry
             x_in = out
         info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] + [1])
-        t_layer = float(np.mean(t_layers))
-        cpu = {"value": round(BATCH / (N_LAYERS * t_layer), 4), "unit": "tokens/s", "cores": int(cores),
-               "kind": "oracle",
-               "sample": f"oracle decode of layers 0-1 of one B={BATCH} step ({t_layer:.2f} s/layer), scaled to 23 layers"}
-        log(f"parity sample ok: {parity}; oracle {t_layer:.2f} s/layer on {cores} threads")
+        blas_threads = max([i.get("num_threads", 1) for i in info] + [1])
+        n_cpu, affinity, model = host_cpu()
+        t_layer = float(np.median(t_layers))
+        cpu = {"value": round(BATCH / (N_LAYERS * t_layer), 4), "unit": "tokens/s", "cores": int(blas_threads),
+               "kind": "oracle", "host_cpus": n_cpu, "cpus_available": affinity, "cpu_model": model,
+               "sample": f"oracle decode of layers 0-1 of one B={BATCH} step ({t_layer:.2f} s/layer), scaled to 23 "
+                         f"layers; cores = the BLAS threads its float64 matmuls used (the rest is single-threaded)"}
+        log(f"parity sample ok: {parity}; oracle {t_layer:.2f} s/layer on {blas_threads} BLAS threads "
+            f"({affinity} of {n_cpu} CPUs available, {model})")
 
     line = {
         "metric": "Mamba2-mixer tokens/s (decode b=8, prefill 512) + % HBM / fp8-MFMA peak",
@@ -403,23 +442,29 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3xe4m3->f32 GEMMs, f32 SSM state, bf16 activations",
+        "dtype": "e4m3 x e4m3 projections (f32 sums), f32 SSM state, bf16 activations",
         "data": "synthetic (seeded; no checkpoint)",
         "config": {"workload": "paged decode, 8 sequences x 1 token through 23 stacked NemotronH Mamba2 mixer "
                                "blocks (hidden 2688, 64 heads x 64, d_state 128, 8 groups), pool of 64 slots",
                    "global_batch": BATCH, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "decode_step_groups_us": [round(u, 1) for u in group_us],
+        "decode_step_median_us": round(float(np.median(group_us)), 1),
         "decode_step_hbm": {"bytes": step_bytes, "achieved_GBs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                             "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_path": decode_path,
         "decode_bf16_state": dec16,
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel (in_proj 10304x2688, m=8)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "us_per_launch": round(gemv_us, 3), "bytes_per_launch": gb},
+                     "us_per_launch": round(gemv_us, 3), "bytes_per_launch": gb,
+                     "repeats_us_per_launch": [round(u / N_LAYERS, 3) for u in pass_all]},
         "prefill_512": {"tokens_per_s": round(T / (pre_us * 1e-6), 1), "us_per_block": round(pre_us, 1),
-                        "gemm": gemm, "gemm_bound": "mfma", "gemm_tflops": round(gemm_tflops, 1),
-                        "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
+                        "repeats_us": pre_all, "path": prefill_path, "gemm": gemm,
+                        "gemm_us": round(blk_gemm_us, 2),
+                        "gemm_frac_of_block": round(blk_gemm_us / pre_us, 3)},
         "gemm_m15360": gemm_large,
-        "prefill_ragged_15360": {"lengths": rl, "us_per_block": round(rag_us, 1),
+        "linear_sweep": sweep,
+        "prefill_ragged_15360": {"lengths": rl, "us_per_block": round(rag_us, 1), "repeats_us": rag_all,
                                  "tokens_per_s": round(RT / (rag_us * 1e-6), 1)},
         "parity_sample": parity,
         "cpu_baseline": cpu,

@@ -13,7 +13,8 @@ import os
 __all__ = ["lib", "LIB_PATH", "NhmError", "Geometry", "Layout", "WsLayout", "Fp8Weight", "MixerParams",
            "GEOMETRY", "mixer_layout", "quantize_static", "fp8_linear", "fp8_linear_workspace_bytes",
            "decode_ws_layout", "prefill_ws_layout", "mixer_decode", "mixer_prefill", "NHM_BF16", "NHM_E4M3",
-           "NHM_F32", "fp8_dequant_channel_bf16", "mixer_decode_noalloc"]
+           "NHM_F32", "fp8_dequant_channel_bf16", "mixer_decode_noalloc", "mixer_decode_q",
+           "dispatch_counters"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnhm.so")
 if not os.path.exists(LIB_PATH):
@@ -47,6 +48,10 @@ class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("total", "q_in", "zxbcdt", "xbc_conv", "y", "norm", "q_out")]
 
 
+class _DispatchCounter(C.Structure):
+    _fields_ = [("kernel", C.c_char_p), ("launches", C.c_uint64), ("rows", C.c_uint64)]
+
+
 class _Fp8Weight(C.Structure):
     _fields_ = [("w", C.c_void_p), ("w_scale", C.c_void_p), ("a_scale", C.c_void_p), ("n", C.c_int64),
                 ("k", C.c_int64)]
@@ -78,6 +83,9 @@ _SIGS = {
                                     _p, _sz, _p]),
     "nhm_mixer_decode_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p, _sz,
                                       _p]),
+    "nhm_dispatch_counters": (C.c_int32, [C.POINTER(_DispatchCounter), C.c_int32, C.c_int32]),
+    "nhm_mixer_decode_q": (C.c_int, [C.POINTER(_MixerParams), _p, _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p, _p,
+                                     _p, _sz, _p]),
     "nhm_mixer_decode_noalloc": (C.c_int, [C.POINTER(_MixerParams), _p, _i32, _p, _p, C.c_int, _p, _i32, _p, _p]),
     "nhm_mixer_prefill_ex": (C.c_int, [C.POINTER(_MixerParams), _p, _i64, _p, _i32, _p, _p, _i32, _p, C.c_int, _p,
                                        _i32, _p, _p, _sz, _p]),
@@ -238,6 +246,27 @@ def mixer_decode(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out
     _check(lib.nhm_mixer_decode_ex(C.byref(params.struct), _ptr(hidden), batch, _ptr(slot_idx), _ptr(ssm_pool),
                                    _ssm_type(ssm_pool), _ptr(conv_pool), int(ssm_pool.shape[0]), _ptr(out), _ptr(ws),
                                    ws.numel(), _stream(stream)))
+    return out
+
+
+def dispatch_counters(reset=False):
+    """{kernel: (launches, rows)} of every kernel launched since the last reset (host-side
+    counters; a launch captured into a graph counts once). reset=True zeroes them after reading."""
+    n = int(lib.nhm_dispatch_counters(None, 0, 0))
+    arr = (_DispatchCounter * n)()
+    lib.nhm_dispatch_counters(arr, n, 1 if reset else 0)
+    return {c.kernel.decode(): (int(c.launches), int(c.rows)) for c in arr if c.launches}
+
+
+def mixer_decode_q(params: MixerParams, hidden, slot_idx, ssm_pool, conv_pool, out, ws, hidden_q=None, out_q=None,
+                   out_q_scale=None, stream=None):
+    """mixer_decode with a pre-quantized input (hidden_q: e4m3 codes under in_proj's a_scale; hidden
+    may then be None) and/or the output's codes (out_q under out_q_scale, a device f32 [1])."""
+    src = hidden if hidden is not None else hidden_q
+    batch = int(src.shape[0])
+    _check(lib.nhm_mixer_decode_q(C.byref(params.struct), _ptr(hidden), _ptr(hidden_q), batch, _ptr(slot_idx),
+                                  _ptr(ssm_pool), _ssm_type(ssm_pool), _ptr(conv_pool), int(ssm_pool.shape[0]),
+                                  _ptr(out), _ptr(out_q), _ptr(out_q_scale), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -22,6 +22,19 @@ nhm_status fail(nhm_status s, const char* fmt, ...) {
     return s;
 }
 
+static const char* const kKernNames[(int)Kern::kCount] = {
+    "quant_vec8", "quant_scalar", "dequant_channel", "gemv", "gemm_ring192x128", "gemm_ring192x128_exact",
+    "gemm_ring256x128", "gemm_ring256x128_exact", "gemm_ring256x256", "gemm_ring256x256_exact", "gemm_panel64x128",
+    "gemm_panel64x128_exact", "gemm_tile128", "gemm_tile128_exact", "gemm_splitk_reduce", "decode_ssm",
+    "gnorm_quant", "conv_fwd", "ssd_state", "ssd_pass", "ssd_out"};
+static std::atomic<uint64_t> g_launches[(int)Kern::kCount];
+static std::atomic<uint64_t> g_rows[(int)Kern::kCount];
+
+void count_launch(Kern k, int64_t rows) {
+    g_launches[(int)k].fetch_add(1, std::memory_order_relaxed);
+    g_rows[(int)k].fetch_add((uint64_t)(rows > 0 ? rows : 0), std::memory_order_relaxed);
+}
+
 nhm_status check_launch(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(NHM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -166,11 +179,15 @@ static MixerWs prefill_ws(const nhm_geometry* g, int64_t T, int32_t n, int32_t c
 // One projection on an e4m3 activation [m, lda]; out_f32 non-null: f32 output instead of out.
 // part / part_bytes: scratch for the GEMM's split-k partials (nullptr: no split).
 // exact: every product summed in f32 on the tiled path too (the GEMV always is).
+// out_q: also the e4m3 codes of the bf16 output under *q_scale (GEMV path only; callers of the
+// tiled path quantize its output themselves).
 static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp8_weight& w, uint16_t* out,
                           int64_t ld_out, hipStream_t st, float* out_f32 = nullptr, float* part = nullptr,
-                          size_t part_bytes = 0, bool exact = false) {
+                          size_t part_bytes = 0, bool exact = false, uint8_t* out_q = nullptr, int64_t ld_q = 0,
+                          const float* q_scale = nullptr) {
     if (use_gemv(m, w.n, w.k))
-        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32);
+        return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, out_q, ld_q,
+                           q_scale);
     return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, part, part_bytes,
                        exact);
 }
@@ -212,6 +229,17 @@ const char* nhm_status_str(nhm_status s) {
 const char* nhm_last_error(void) { return g_err; }
 
 const char* nhm_build_arch(void) { return "gfx950"; }
+
+int32_t nhm_dispatch_counters(nhm_dispatch_counter* out, int32_t max, int32_t reset) {
+    const int32_t n = (int32_t)Kern::kCount;
+    for (int32_t i = 0; i < n; ++i) {
+        const uint64_t l = reset ? g_launches[i].exchange(0, std::memory_order_relaxed)
+                                 : g_launches[i].load(std::memory_order_relaxed);
+        const uint64_t r = reset ? g_rows[i].exchange(0, std::memory_order_relaxed) : g_rows[i].load(std::memory_order_relaxed);
+        if (out && i < max) out[i] = nhm_dispatch_counter{kKernNames[i], l, r};
+    }
+    return n;
+}
 
 nhm_status nhm_mixer_layout(const nhm_geometry* g, nhm_layout* out) {
     g_err[0] = 0;
@@ -397,9 +425,13 @@ static nhm_status device_scratch(hipStream_t st, void** out) {
 }
 
 // nhm_mixer_decode_ex; noalloc: the workspace is this library's device scratch (ws ignored).
-static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
-                              const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
-                              int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream, bool noalloc) {
+// hidden_q (optional): the block input's e4m3 codes under in_proj's activation scale, used
+// instead of quantizing hidden (which may then be NULL). out_q (optional): the codes of the
+// bf16 block output under *out_q_scale.
+static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden, const uint8_t* hidden_q,
+                              int32_t batch, const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type,
+                              uint16_t* conv_pool, int32_t n_slots, uint16_t* out, uint8_t* out_q,
+                              const float* out_q_scale, void* ws, size_t ws_bytes, void* stream, bool noalloc) {
     g_err[0] = 0;
     if (ssm_type != NHM_F32 && ssm_type != NHM_BF16)
         return fail(NHM_ERR_UNSUPPORTED, "SSM state dtype %d: f32 or bf16", (int)ssm_type);
@@ -409,11 +441,13 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
     if (batch < 0) return fail(NHM_ERR_SHAPE, "negative batch");
     if (batch == 0) return NHM_OK;
     if (n_slots <= 0) return fail(NHM_ERR_SHAPE, "n_slots must be positive");
-    if (!hidden || !slot_idx || !ssm_pool || !conv_pool || !out || (!noalloc && !ws))
-        return fail(NHM_ERR_NULL, "hidden, slot_idx, pools, out or ws is NULL");
-    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
-        !aligned(slot_idx, 4) || (!noalloc && !aligned(ws, 256)))
-        return fail(NHM_ERR_ALIGN, "hidden, out and pools must be 16-byte aligned, ws 256-byte aligned");
+    if ((!hidden && !hidden_q) || !slot_idx || !ssm_pool || !conv_pool || !out || (!noalloc && !ws))
+        return fail(NHM_ERR_NULL, "hidden (or its codes), slot_idx, pools, out or ws is NULL");
+    if (out_q && !out_q_scale) return fail(NHM_ERR_NULL, "out_q needs out_q_scale");
+    if ((hidden && !aligned(hidden, 16)) || !aligned(out, 16) || !aligned(ssm_pool, 16) || !aligned(conv_pool, 16) ||
+        !aligned(slot_idx, 4) || (!noalloc && !aligned(ws, 256)) || (hidden_q && !aligned(hidden_q, 16)) ||
+        (out_q && !aligned(out_q, 16)) || (out_q_scale && !aligned(out_q_scale, 4)))
+        return fail(NHM_ERR_ALIGN, "hidden, its codes, out, out_q and pools must be 16-byte aligned, ws 256-byte aligned");
     const MixerWs w = decode_ws(&p->g, batch);
     if (noalloc && w.pub.total > kNoAllocScratchBytes)
         return fail(NHM_ERR_WORKSPACE, "batch %d needs %zu bytes of scratch; the library's per-device scratch holds %zu",
@@ -427,13 +461,17 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
     if (noalloc && (s = device_scratch(st, &ws)) != NHM_OK) return s;
     char* wsb = static_cast<char*>(ws);
     const int64_t H = p->g.hidden;
-    uint8_t* q_in = reinterpret_cast<uint8_t*>(wsb + w.pub.q_in);
+    const uint8_t* q_in = reinterpret_cast<uint8_t*>(wsb + w.pub.q_in);
     uint16_t* zx = reinterpret_cast<uint16_t*>(wsb + w.pub.zxbcdt);
     uint16_t* xc = reinterpret_cast<uint16_t*>(wsb + w.pub.xbc_conv);
     uint8_t* q_out = reinterpret_cast<uint8_t*>(wsb + w.pub.q_out);
 
-    launch_quantize(hidden, batch, H, H, p->in_proj.a_scale, q_in, H, st);
-    if ((s = check_launch("decode quant")) != NHM_OK) return s;
+    if (hidden_q) {
+        q_in = hidden_q;   // pre-quantized by the caller (e.g. the previous block's out_q)
+    } else {
+        launch_quantize(hidden, batch, H, H, p->in_proj.a_scale, const_cast<uint8_t*>(q_in), H, st);
+        if ((s = check_launch("decode quant")) != NHM_OK) return s;
+    }
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
         s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, st);
@@ -477,12 +515,21 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
     // B = 32 two GEMV launches stay ahead (60.0 against 61.6 us). in_proj stays on the GEMV per
     // 16 rows: its exact f32 sums feed dt, which every later decay exponentiates (the GEMM's
     // coarser sums would need the dt recompute the prefill runs).
-    if (batch > 32)
-        return project(q_out, l.d_inner, batch, p->out_proj, out, H, st, nullptr,
-                       reinterpret_cast<float*>(wsb + w.part), w.part_bytes);
+    if (batch > 32) {
+        if ((s = project(q_out, l.d_inner, batch, p->out_proj, out, H, st, nullptr,
+                         reinterpret_cast<float*>(wsb + w.part), w.part_bytes)) != NHM_OK)
+            return s;
+        if (out_q) {   // the tiled path has no code epilogue
+            launch_quantize(out, batch, H, H, out_q_scale, out_q, H, st);
+            return check_launch("decode out_q");
+        }
+        return NHM_OK;
+    }
+    // up to 32 rows: the GEMV, which also writes the codes of its bf16 output when asked
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, st);
+        s = project(q_out + (int64_t)r0 * l.d_inner, l.d_inner, mg, p->out_proj, out + (int64_t)r0 * H, H, st, nullptr,
+                    nullptr, 0, false, out_q ? out_q + (int64_t)r0 * H : nullptr, H, out_q_scale);
         if (s != NHM_OK) return s;
     }
     return NHM_OK;
@@ -495,15 +542,23 @@ extern "C" {
 nhm_status nhm_mixer_decode_ex(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
                                const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
                                int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-    return decode_call(p, hidden, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, ws, ws_bytes, stream,
-                       false);
+    return decode_call(p, hidden, nullptr, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, nullptr,
+                       nullptr, ws, ws_bytes, stream, false);
+}
+
+nhm_status nhm_mixer_decode_q(const nhm_mixer_params* p, const uint16_t* hidden, const uint8_t* hidden_q, int32_t batch,
+                              const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
+                              int32_t n_slots, uint16_t* out, uint8_t* out_q, const float* out_q_scale, void* ws,
+                              size_t ws_bytes, void* stream) {
+    return decode_call(p, hidden, hidden_q, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, out_q,
+                       out_q_scale, ws, ws_bytes, stream, false);
 }
 
 nhm_status nhm_mixer_decode_noalloc(const nhm_mixer_params* p, const uint16_t* hidden, int32_t batch,
                                     const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type, uint16_t* conv_pool,
                                     int32_t n_slots, uint16_t* out, void* stream) {
-    return decode_call(p, hidden, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, nullptr, 0, stream,
-                       true);
+    return decode_call(p, hidden, nullptr, batch, slot_idx, ssm_pool, ssm_type, conv_pool, n_slots, out, nullptr,
+                       nullptr, nullptr, 0, stream, true);
 }
 
 nhm_status nhm_mixer_prefill(const nhm_mixer_params* p, const uint16_t* hidden, int64_t n_tokens,

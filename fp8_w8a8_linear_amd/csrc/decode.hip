@@ -144,6 +144,7 @@ nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st) {
         decode_ssm_kernel<true><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
     else
         decode_ssm_kernel<false><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
+    count_launch(Kern::kDecodeSsm, m);
     return check_launch("decode_ssm");
 }
 

@@ -843,6 +843,7 @@ template <int BM, int WN, bool kExact>
 static void launch_panel(const GemmArgs& g, hipStream_t st) {
     const int64_t npan = (g.n + 4 * WN - 1) / (4 * WN), nmt = (g.m + BM - 1) / BM;
     panel_kernel<BM, WN, kExact><<<dim3((unsigned)(8 * nmt * ((npan + 7) / 8))), dim3(256), 0, st>>>(g);
+    count_launch(kExact ? Kern::kPanel64x128Exact : Kern::kPanel64x128, g.m);
 }
 
 // Measured on MI355X at m = 512 (in_proj 10304 x 2688, out_proj 2688 x 4096): the
@@ -906,9 +907,11 @@ static nhm_status dispatch_gemm(GemmArgs g, hipStream_t st, float* part, size_t 
         const int64_t c192 = t192 >= 160 ? ((t192 + 255) / 256) * (192 + 128) : INT64_MAX;
         if (c192 < c256) {
             ring128_kernel<192, 128, kExact><<<dim3((unsigned)t192), dim3(512), 0, st>>>(g);
+            count_launch(kExact ? Kern::kRing192x128Exact : Kern::kRing192x128, m);
             return check_launch("gemm (192 x 128)");
         }
         tile256_kernel<256, 128, kExact><<<dim3((unsigned)half_tiles), dim3(512), 0, st>>>(g);
+        count_launch(kExact ? Kern::kRing256x128Exact : Kern::kRing256x128, m);
         return check_launch("gemm (256 x 128)");
     }
     if (m <= 640 && offsets_fit) {   // too few ring tiles to fill the chip
@@ -917,9 +920,11 @@ static nhm_status dispatch_gemm(GemmArgs g, hipStream_t st, float* part, size_t 
             g.ksplit = S;
             g.part = part;
             ring128_kernel<192, 128, kExact><<<dim3((unsigned)(t192 * S)), dim3(512), 0, st>>>(g);
+            count_launch(kExact ? Kern::kRing192x128Exact : Kern::kRing192x128, m);
             nhm_status s = check_launch("gemm (192 x 128, split k)");
             if (s != NHM_OK) return s;
             splitk_reduce_kernel<<<dim3((unsigned)((m * n + 1023) / 1024)), dim3(256), 0, st>>>(g);
+            count_launch(Kern::kSplitkReduce, m);
             return check_launch("gemm split-k reduce");
         }
         launch_panel<64, 32, kExact>(g, st);
@@ -928,12 +933,14 @@ static nhm_status dispatch_gemm(GemmArgs g, hipStream_t st, float* part, size_t 
     const int64_t wide_tiles = ((n + kWT - 1) / kWT) * ((m + kWT - 1) / kWT);
     if (offsets_fit && wide_tiles >= 160) {
         tile256_kernel<256, 256, kExact><<<dim3((unsigned)wide_tiles), dim3(512), 0, st>>>(g);
+        count_launch(kExact ? Kern::kRing256x256Exact : Kern::kRing256x256, m);
         return check_launch("gemm (256 x 256)");
     }
     if (!offsets_fit)   // refused by the callers' host checks before anything is enqueued
         return fail(NHM_ERR_UNSUPPORTED, "gemm: an operand of 2 GiB or more");
     const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));
     gemm_kernel<kExact><<<grid, dim3(256), 0, st>>>(g);
+    count_launch(kExact ? Kern::kTile128Exact : Kern::kTile128, m);
     return check_launch("gemm");
 }
 

@@ -25,6 +25,9 @@ struct GemvArgs {
     const uint8_t* w; const float* w_scale; const float* a_scale; int64_t n, k;
     uint16_t* out; int64_t ld_out; bool vec_out;   // vec_out: rows aligned for 4-element stores
     float* out_f32;                                 // non-null: f32 output [m, ld_out] instead of out
+    // non-null (bf16 output only): also the e4m3 codes of the bf16 output, E4M3(out / *q_scale),
+    // at out_q[m * ld_q + n] -- the next projection's pre-quantized input
+    uint8_t* out_q; int64_t ld_q; const float* q_scale; bool vec_q;
     int ksteps;
     int rows;                                       // features per workgroup, a multiple of 4 up to 16 x kTiles
 };
@@ -54,6 +57,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     // First the scales of the epilogue (so that waiting for them later does not wait for the
     // weight stream), then the weight stream, k-step by k-step.
     const float sa = *g.a_scale;
+    const float sq = g.out_q ? *g.q_scale : 1.0f;
     float sc[kTiles][4];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
@@ -141,13 +145,27 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
             for (int r = 0; r < 4; ++r)
                 if (nb + r < nend) o[r] = (uint16_t)hb[r];
         }
+        if (g.out_q) {   // the static quant of the bf16 values just stored (IEEE quotient)
+            const uint32_t c4 = quant_bf16x4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), sq);
+            uint8_t* oq = g.out_q + (int64_t)col * g.ld_q + nb;
+            if (g.vec_q && nb + 3 < nend) {
+                *reinterpret_cast<uint32_t*>(oq) = c4;
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < nend) oq[r] = (uint8_t)(c4 >> (8 * r));
+            }
+        }
     }
 }
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
-                       float* out_f32) {
+                       float* out_f32, uint8_t* out_q, int64_t ld_q, const float* q_scale) {
     GemvArgs g;
+    g.out_q = out_f32 ? nullptr : out_q;
+    g.ld_q = ld_q;
+    g.q_scale = q_scale;
+    g.vec_q = ld_q % 4 == 0 && reinterpret_cast<uintptr_t>(out_q) % 4 == 0;
     g.a = a; g.lda = lda; g.m = m;
     g.w = w; g.w_scale = w_scale; g.a_scale = a_scale; g.n = n; g.k = k;
     g.out = out; g.ld_out = ld_out;
@@ -198,6 +216,7 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     }
 #undef NHM_GEMV_STEPS
 #undef NHM_GEMV_LAUNCH
+    count_launch(Kern::kGemv, m);
     return check_launch("gemv");
 }
 

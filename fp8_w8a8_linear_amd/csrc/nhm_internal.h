@@ -17,6 +17,16 @@ nhm_status check_launch(const char* what);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Path-taken counters (nhm_dispatch_counters): one per kernel the library launches, counting
+// launches and the rows (tokens, or chunks for the scan kernels) they covered. Host-side,
+// atomic; a launch recorded into a HIP graph counts once, at capture.
+enum class Kern : int {
+    kQuantVec8, kQuantScalar, kDequantChannel, kGemv, kRing192x128, kRing192x128Exact, kRing256x128,
+    kRing256x128Exact, kRing256x256, kRing256x256Exact, kPanel64x128, kPanel64x128Exact, kTile128,
+    kTile128Exact, kSplitkReduce, kDecodeSsm, kGnormQuant, kConvFwd, kSsdState, kSsdPass, kSsdOut, kCount
+};
+void count_launch(Kern k, int64_t rows);
+
 // ---- activation quant (quant.hip)
 void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                      uint8_t* q, int64_t ld_q, hipStream_t st);
@@ -29,10 +39,11 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
 
 // out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda], stored to
 // out[m * ld_out + n]; with out_f32 the unrounded f32 result goes to out_f32[m * ld_out + n]
-// instead.
+// instead. out_q (bf16 output only): also E4M3(out / *q_scale) at out_q[m * ld_q + n].
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
-                       float* out_f32 = nullptr);
+                       float* out_f32 = nullptr, uint8_t* out_q = nullptr, int64_t ld_q = 0,
+                       const float* q_scale = nullptr);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 // part (16-byte aligned, part_bytes >= gemm_part_bytes(m, n, k)): scratch for the split-k

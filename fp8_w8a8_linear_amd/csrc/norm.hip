@@ -129,6 +129,7 @@ nhm_status launch_gnorm_quant(const GnormArgs& a, hipStream_t st) {
     else if (gw <= 1024) gnorm_quant_kernel<2><<<grid, 256, 0, st>>>(a);
     else if (gw <= 2048) gnorm_quant_kernel<4><<<grid, 256, 0, st>>>(a);
     else gnorm_quant_kernel<0><<<grid, 256, 0, st>>>(a);
+    count_launch(Kern::kGnormQuant, a.T);
     return check_launch("gnorm_quant");
 }
 

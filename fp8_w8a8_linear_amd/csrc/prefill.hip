@@ -237,12 +237,14 @@ nhm_status launch_prefill_mid(const PrefillArgs& a, hipStream_t st) {
     const int c8_blocks = (a.conv_dim / 8 + 255) / 256;
     const int64_t tblocks = (a.T + kConvRun - 1) / kConvRun;
     conv_fwd_kernel<<<dim3((unsigned)(1 + c8_blocks * tblocks)), 256, 0, st>>>(a, c8_blocks);
+    count_launch(Kern::kConvFwd, a.T);
     if (a.max_chunks > 0) launch_ssd_state(a, st);
     if (a.n_seqs > 0) {
         if (a.ssm_pool_bf16)
             ssd_pass_kernel<true><<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
         else
             ssd_pass_kernel<false><<<dim3(a.n_seqs, a.n_heads, kHP / 8), 256, 0, st>>>(a);
+        count_launch(Kern::kSsdPass, a.max_chunks);
     }
     if (a.max_chunks > 0) launch_ssd_out(a, st);
     nhm_status s = check_launch("prefill");

@@ -72,6 +72,7 @@ void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x
         quant_vec8_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, rows, cols / 8, ld_x, scale, q, ld_q);
     else
         quant_scalar_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, rows, cols, ld_x, scale, q, ld_q);
+    count_launch(vec ? Kern::kQuantVec8 : Kern::kQuantScalar, rows);
 }
 
 }  // namespace nhm
@@ -116,6 +117,7 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
     if (blocks > 256 * 16) blocks = 256 * 16;
     dequant_channel_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, rows, cols / 16, ld_w, w_scale, out,
                                                                         ld_out);
+    count_launch(Kern::kDequantChannel, rows);
 }
 
 }  // namespace nhm

@@ -369,10 +369,12 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
 
 void launch_ssd_state(const PrefillArgs& a, hipStream_t st) {
     ssd_state_kernel<<<dim3((unsigned)(a.max_chunks * a.n_heads)), kThreads, 0, st>>>(a);
+    count_launch(Kern::kSsdState, a.max_chunks);
 }
 
 void launch_ssd_out(const PrefillArgs& a, hipStream_t st) {
     ssd_out_kernel<<<dim3((unsigned)(a.max_chunks * a.n_heads)), kThreads, 0, st>>>(a);
+    count_launch(Kern::kSsdOut, a.max_chunks);
 }
 
 }  // namespace nhm

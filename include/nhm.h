@@ -15,8 +15,9 @@
  *
  * Conventions that hold for every entry point:
  *   - Pointers marked (device) address GPU memory; (host) address host memory.
- *     The caller owns every buffer. The library allocates nothing, keeps no cache and
- *     no state between calls, never synchronizes the device, and only enqueues work
+ *     The caller owns every buffer. The library allocates nothing (but the fixed scratch of
+ *     nhm_mixer_decode_noalloc), keeps no cache and no state between calls (but the
+ *     diagnostic dispatch counters), never synchronizes the device, and only enqueues work
  *     on the given stream (a hipStream_t; NULL = the default stream). All calls are
  *     therefore legal inside HIP graph capture.
  *   - Shapes, null pointers, alignment and geometry are validated on the host before
@@ -81,6 +82,20 @@ NHM_API const char* nhm_last_error(void);
 
 /* Name of the GPU architecture the library was built for ("gfx950"). */
 NHM_API const char* nhm_build_arch(void);
+
+/* Path-taken counters ([PR1289] commit log: the device path is told from the host path by
+ * its own dispatch counters -- state-update rows, chunk-scan calls, conv calls): for each
+ * kernel the library launches, the launches and the rows they covered (tokens; chunks for the
+ * chunked-scan kernels) since the counters were last reset. Host-side and atomic, the only
+ * state the library keeps; a launch recorded into a HIP graph counts once, at capture, not
+ * per replay. Fills out[0 .. min(max, count) - 1] (host; out may be NULL), zeroes the counters
+ * when reset != 0, and returns the number of counters. Names are static strings. */
+typedef struct nhm_dispatch_counter {
+    const char* kernel;
+    uint64_t launches;
+    uint64_t rows;
+} nhm_dispatch_counter;
+NHM_API int32_t nhm_dispatch_counters(nhm_dispatch_counter* out, int32_t max, int32_t reset);
 
 /* ---------------------------------------------------------------- geometry */
 
@@ -287,6 +302,26 @@ NHM_API nhm_status nhm_mixer_decode(const nhm_mixer_params* p, const uint16_t* h
                             const int32_t* slot_idx, float* ssm_pool, uint16_t* conv_pool,
                             int32_t n_slots, uint16_t* out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* nhm_mixer_decode_ex with the block input pre-quantized and the block output's codes emitted,
+ * so that stacked blocks pass e4m3 codes along instead of re-quantizing each block's input in
+ * a launch of its own ([PR972] "Correspondence with dense_nvfp4_gemm.h": the GEMM seam takes a
+ * pre-quantized activation; [PR1288] "What it does": each block's in_proj quantizes its input
+ * with its static input_scale).
+ *   hidden    (device) bf16 [batch, hidden] or NULL when hidden_q is given
+ *   hidden_q  (device) e4m3 [batch, hidden], 16-byte aligned, or NULL: the codes
+ *             E4M3(hidden / *p->in_proj.a_scale) (e.g. the previous block's out_q under this
+ *             block's in_proj a_scale); used instead of quantizing hidden
+ *   out_q     (device) e4m3 [batch, hidden], 16-byte aligned, or NULL: receives
+ *             E4M3(out / *out_q_scale) of the bf16 block output (written by the out_proj
+ *             epilogue up to 32 rows, by a quant launch above)
+ *   out_q_scale (device) f32 [1]; required with out_q (the next block's in_proj a_scale)
+ * out, the pools and everything else are those of nhm_mixer_decode_ex; with hidden_q given,
+ * the workspace's q_in region is left as it was. Errors: those of nhm_mixer_decode_ex. */
+NHM_API nhm_status nhm_mixer_decode_q(const nhm_mixer_params* p, const uint16_t* hidden, const uint8_t* hidden_q,
+                              int32_t batch, const int32_t* slot_idx, void* ssm_pool, nhm_dtype ssm_type,
+                              uint16_t* conv_pool, int32_t n_slots, uint16_t* out, uint8_t* out_q,
+                              const float* out_q_scale, void* ws, size_t ws_bytes, void* stream);
 
 /* nhm_mixer_decode_ex without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -24,9 +24,23 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(nhm):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(nhm.lib, n), f"{n} not exported"
+
+
+def test_dispatch_counters(nhm):
+    """Every kernel has a named counter; refused calls launch nothing and count nothing."""
+    n = nhm.lib.nhm_dispatch_counters(None, 0, 1)
+    assert n >= 21
+    arr = (nhm._DispatchCounter * n)()
+    assert nhm.lib.nhm_dispatch_counters(arr, n, 0) == n
+    names = [c.kernel.decode() for c in arr]
+    assert len(set(names)) == n and "gemv" in names and "decode_ssm" in names and "ssd_out" in names
+    assert all(c.launches == 0 and c.rows == 0 for c in arr)
+    q = nhm.lib.nhm_fp8_quantize_static
+    assert q(0x101, 2, 8, 8, 0x100, 0x200, 8, None) == 3
+    assert nhm.dispatch_counters() == {}
 
 
 def test_build_arch(nhm):
@@ -184,6 +198,25 @@ def test_decode_refusals(nhm):
     p = _params(nhm)
     p.g = g
     assert call(p=p) == 4
+
+
+def test_decode_q_refusals(nhm):
+    """The pre-quantized decode: it needs the input (bf16 or codes), and out_q needs its scale."""
+    f = nhm.lib.nhm_mixer_decode_q
+    need = nhm.decode_ws_layout(8)["total"]
+    H, Q, SL, SP, CP, O, OQ, S, WS = [0x100000 * i for i in range(1, 10)]
+    p = _params(nhm)
+
+    def call(hidden=H, hq=Q, out_q=OQ, scale=S, wsb=need):
+        return f(C.byref(p), hidden, hq, 8, SL, SP, nhm.NHM_F32, CP, 64, O, out_q, scale, WS, wsb, None)
+
+    assert call(hidden=None, hq=None) == 1
+    assert call(scale=None) == 1
+    assert call(hq=Q + 8) == 3
+    assert call(out_q=OQ + 4) == 3
+    assert call(scale=S + 2) == 3
+    assert call(wsb=need - 1) == 5
+    assert f(C.byref(p), H, Q, 0, SL, SP, nhm.NHM_F32, CP, 64, O, OQ, S, WS, need, None) == 0
 
 
 def test_decode_noalloc_refusals(nhm):

@@ -184,6 +184,54 @@ def test_decode_stacked_layers(nhm):
         x, xd = got, out                                # next layer input: this layer's bf16 output
 
 
+# 8 rows: the out_proj GEMV writes the codes in its epilogue; 40 rows: the tiled out_proj and a
+# quant launch
+@pytest.mark.parametrize("B", [8, 40])
+def test_decode_chained_codes(nhm, B):
+    """Three stacked blocks passing e4m3 codes (nhm_mixer_decode_q: each block's out_q, under
+    the next block's in_proj scale, is the next block's hidden_q) against the same blocks through
+    nhm_mixer_decode with bf16 input and output: outputs, state and conv pools bit-identical, and
+    every out_q equal to the oracle's quantizer applied to the GPU's bf16 output."""
+    from oracle import quantize_static
+    from tests.gpu_util import dev, host, upload_params, zeros_ws
+    from workloads import block_params, conv_pool, hidden, slots, ssm_pool
+    S, L = 64, 3
+    sl = dev(slots(2, B, S))
+    x = dev(hidden(2, B, extra=70 + B))
+    ps = [block_params(2, layer) for layer in range(L)]
+    pds = [upload_params(p) for p in ps]
+    ws = zeros_ws(nhm.decode_ws_layout(B)["total"])
+    pools = [(ssm_pool(2, layer, S), conv_pool(2, layer, S)) for layer in range(L)]
+    runs = []
+    for chained in (False, True):
+        xin, qin, outs, qs, st = x, None, [], [], []
+        for layer in range(L):
+            sp, cp = dev(pools[layer][0]), dev(pools[layer][1])
+            out = torch.empty((B, H), dtype=torch.int16, device="cuda")
+            if chained:
+                oq = torch.full((B, H), 0x5A, dtype=torch.uint8, device="cuda") if layer + 1 < L else None
+                nxt = pds[layer + 1].in_proj.a_scale if layer + 1 < L else None
+                nhm.mixer_decode_q(pds[layer], xin if layer == 0 else None, sl, sp, cp, out, ws,
+                                   hidden_q=qin, out_q=oq, out_q_scale=nxt)
+                qin = oq
+                qs.append(oq)
+            else:
+                nhm.mixer_decode(pds[layer], xin, sl, sp, cp, out, ws)
+            torch.cuda.synchronize()
+            outs.append(host(out))
+            st.append((host(sp), host(cp)))
+            xin = out
+        runs.append((outs, st, qs))
+    (o_plain, s_plain, _), (o_chain, s_chain, q_chain) = runs
+    for layer in range(L):
+        assert np.array_equal(o_plain[layer], o_chain[layer]), f"layer {layer}: outputs differ"
+        assert np.array_equal(s_plain[layer][0], s_chain[layer][0]), f"layer {layer}: state pools differ"
+        assert np.array_equal(s_plain[layer][1], s_chain[layer][1]), f"layer {layer}: conv pools differ"
+        if layer + 1 < L:
+            want = quantize_static(o_chain[layer], ps[layer + 1]["in_a_scale"])
+            assert np.array_equal(host(q_chain[layer]), want), f"layer {layer}: out_q codes"
+
+
 def test_decode_deterministic(nhm, block0):
     from tests.gpu_util import upload_params
     from workloads import conv_pool, hidden, ssm_pool
