@@ -29,7 +29,9 @@ struct GemvArgs {
     // at out_q[m * ld_q + n] -- the next projection's pre-quantized input
     uint8_t* out_q; int64_t ld_q; const float* q_scale; bool vec_q;
     int ksteps;
-    int rows;                                       // features per workgroup, a multiple of 4 up to 16 x kTiles
+    // workgroup b owns features [b base + min(b, extra), ...) -- base + 1 of them for b < extra,
+    // base for the others (at most 16 x kTiles)
+    int base, extra;
 };
 
 // Cache policy of the weight stream: the default. The non-temporal hint (nt) made the in_proj
@@ -41,8 +43,9 @@ template <int kWaves, int kSteps, int kTiles>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves - 1][kTiles][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * g.rows;
-    const int64_t nend = n0 + g.rows < g.n ? n0 + g.rows : g.n;   // this workgroup's features end
+    const int b = blockIdx.x;
+    const int64_t n0 = (int64_t)b * g.base + (b < g.extra ? b : g.extra);
+    const int64_t nend = n0 + g.base + (b < g.extra ? 1 : 0);   // this workgroup's features end
     const int col = lane & 15;                  // B operand column (token)
     const int kq = (lane >> 4) * 32;
     // MFMA row tile t covers features n0 + 16 t .. + 15 (A operand row lane % 16; rows at or
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         if (nb >= nend) break;   // row tiles are in feature order
         if (g.out_f32) {
             float* of = g.out_f32 + (int64_t)col * g.ld_out + nb;
-            if (g.vec_out && nb + 3 < nend) {
+            if (g.vec_out && (nb & 3) == 0 && nb + 3 < nend) {
                 *reinterpret_cast<float4*>(of) =
                     make_float4(acc[t][0] * sc[t][0], acc[t][1] * sc[t][1], acc[t][2] * sc[t][2], acc[t][3] * sc[t][3]);
             } else {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[t][r] * sc[t][r]);
         uint16_t* o = g.out + (int64_t)col * g.ld_out + nb;
-        if (g.vec_out && nb + 3 < nend) {
+        if (g.vec_out && (nb & 3) == 0 && nb + 3 < nend) {
             *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         } else {
             for (int r = 0; r < 4; ++r)
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         if (g.out_q) {   // the static quant of the bf16 values just stored (IEEE quotient)
             const uint32_t c4 = quant_bf16x4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), sq);
             uint8_t* oq = g.out_q + (int64_t)col * g.ld_q + nb;
-            if (g.vec_q && nb + 3 < nend) {
+            if (g.vec_q && (nb & 3) == 0 && nb + 3 < nend) {
                 *reinterpret_cast<uint32_t*>(oq) = c4;
             } else {
                 for (int r = 0; r < 4; ++r)
@@ -182,21 +185,21 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     const int waves = g.ksteps < 24 ? 4 : (g.ksteps <= 8 * kGemvMaxSteps ? 8 : 16);
     const int per = (g.ksteps + waves - 1) / waves;
     const int steps = per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
-    // Features per workgroup: a multiple of 4 (whole 4-feature stores) up to 16 per MFMA row
-    // tile, 3 tiles (48) where each wave holds few enough k-steps (4 waves), else 1. Each CU
-    // streams its share at a rate bounded by the requests it keeps in flight, so the choice
-    // minimises the operand bytes the busiest CU pulls: (workgroups per CU) x (features +
-    // tokens) x k -- every workgroup reads its weight rows and the whole activation. The spare
-    // MFMA rows of a tile load zeros.
+    // Features per workgroup: up to 16 per MFMA row tile, 3 tiles (48) where each wave holds
+    // few enough k-steps (4 waves), else 1. Each CU streams its share at a rate bounded by the
+    // requests it keeps in flight, so the split minimises the operand bytes the busiest CU pulls,
+    // (features + tokens) x k -- every workgroup reads its weight rows and the whole activation:
+    // the features are dealt evenly over one workgroup per CU (256; in_proj at m = 8: 40-41
+    // features each, against 44 on 235 CUs with whole multiples of 4), or over as many as the
+    // tile limit needs, and never fewer than 4 per workgroup. The spare MFMA rows of a tile load
+    // zeros; features that do not start a 4-aligned run are stored one at a time.
     const int max_rows = waves == 4 ? 48 : 16;
-    int64_t best = INT64_MAX;
-    for (int r = 4; r <= max_rows; r += 4) {
-        const int64_t wgs = (n + r - 1) / r;
-        const int64_t cost = (wgs + 255) / 256 * (r + m);
-        if (cost < best) { best = cost; g.rows = r; }
-    }
-    const int tiles = (g.rows + 15) / 16;
-    const dim3 grid((unsigned)((n + g.rows - 1) / g.rows));
+    int64_t wgs = (n + 3) / 4 < 256 ? (n + 3) / 4 : 256;
+    if ((n + wgs - 1) / wgs > max_rows) wgs = (n + max_rows - 1) / max_rows;
+    g.base = (int)(n / wgs);
+    g.extra = (int)(n % wgs);
+    const int tiles = (g.base + (g.extra ? 1 : 0) + 15) / 16;
+    const dim3 grid((unsigned)wgs);
 #define NHM_GEMV_LAUNCH(W, S, T) gemv_kernel<W, S, T><<<grid, dim3(W * 64), 0, st>>>(g)
 #define NHM_GEMV_STEPS(W, T)                         \
     do {                                             \

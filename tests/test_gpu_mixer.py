@@ -620,3 +620,72 @@ def test_prefill_small_geometry(nhm):
     _check_states(host(spd), spr, sp, touched)
     _check_windows(host(cpd), cpr, cp, touched)
     print(f"prefill small geometry {lens}: {m}")
+
+
+def _edge_params():
+    """Block 0's parameters with the method's corner cases switched on: heads 0-7 have
+    dt_raw + dt_bias > 20 (softplus taken as its argument), head 8 A_log = 0 (A = -1) and head 9
+    A_log = ln 16 (A = -16), the two ends of the A_log draw."""
+    from workloads import block_params
+    p = {k: (v.copy() if hasattr(v, "copy") else v) for k, v in block_params(0, 0).items()}
+    p["dt_bias"][:8] = np.float32(25.0)
+    p["A_log"][8] = np.float32(0.0)
+    p["A_log"][9] = np.float32(np.log(16.0))
+    return p
+
+
+def _edge_hidden(T, extra):
+    """Block input with a tenth of its entries scaled to |x| in [4, 2000]: |x| / s >= 448 for
+    the static scale s = 4/448, so those codes saturate at +-448."""
+    from workloads import bf16_bits
+    r = np.random.default_rng(9000 + extra)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    big = r.random((T, H)) < 0.1
+    x[big] = np.sign(x[big]) * r.uniform(4.0, 2000.0, int(big.sum())).astype(np.float32)
+    return bf16_bits(x)
+
+
+def test_decode_edge_cases(nhm):
+    """Decode B=8 with the softplus linear branch, both ends of A_log and saturating inputs."""
+    from oracle import mixer_decode, quantize_static
+    from tests.gpu_util import upload_params, ws_region
+    from workloads import conv_pool, ssm_pool, slots
+    p = _edge_params()
+    B, S = 8, 16
+    h = _edge_hidden(B, 1)
+    assert np.sum(quantize_static(h, p["in_a_scale"]) & 0x7f == 0x7e) > 1000     # saturated codes present
+    sl = slots(2, B, S)
+    sp, cp = ssm_pool(2, 5, S), conv_pool(2, 5, S)
+    out, spg, cpg, ws, lay = _gpu_decode(nhm, upload_params(p), h, sl, sp, cp)
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_decode(p, h, sl, spr, cpr)
+    assert np.array_equal(ws_region(ws, lay["q_in"], B * H, np.uint8).reshape(B, H), res["q_in"].reshape(B, H))
+    m = _parity(out, ws, lay, list(range(B)), ref, res["norm"], res["q_out"], p)
+    st = _check_states(spg, spr, sp, set(int(s) for s in sl))
+    _check_windows(cpg, cpr, cp, set(int(s) for s in sl))
+    print(f"decode edge cases: {m}, state rel l2 {st:.3e}")
+
+
+def test_prefill_edge_cases(nhm):
+    """Prefill of a 100-token sequence from a carried state and a fresh 3-token one with the same
+    corner cases (under 128 tokens: the whole-call bar applies)."""
+    from oracle import mixer_prefill
+    from tests.gpu_util import upload_params
+    from workloads import conv_pool, ssm_pool
+    p = _edge_params()
+    lens, has_init, S = [100, 3], [1, 0], 4
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    h = _edge_hidden(T, 2)
+    sl = np.array([2, 0], np.int32)
+    sp, cp = ssm_pool(3, 5, S), conv_pool(3, 5, S)
+    out, spg, cpg, ws, lay = _gpu_prefill(nhm, upload_params(p), h, cu, sl, has_init, sp, cp)
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_prefill(p, h, cu, sl, has_init, spr, cpr)
+    norm, q, qin = _prefill_refs(res, lens)
+    from tests.gpu_util import ws_region
+    assert np.array_equal(ws_region(ws, lay["q_in"], T * H, np.uint8), qin.reshape(-1))
+    m = _parity(out, ws, lay, list(range(T)), ref, norm, q, p)
+    st = _check_states(spg, spr, sp, set(int(s) for s in sl))
+    _check_windows(cpg, cpr, cp, set(int(s) for s in sl))
+    print(f"prefill edge cases: {m}, state rel l2 {st:.3e}")
