@@ -662,16 +662,33 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     };
 #pragma unroll
     for (int s = 0; s < kRing - 1; ++s) issue(s);
-    v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
-    wait_vmcnt<(kRing - 2) * kLoads>();
-    __syncthreads();
-    read_ops(0, w0, a0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        step(kt, w0, a0, w1, a1);
-        step(kt + 1, w1, a1, w0, a0);
+    if constexpr (kExact && TM == 256) {
+        // Exact sums on the 256 x 256 tile: the 128 accumulators, one stage's operands and the
+        // converted runs fill a wave's 256 registers, so each stage's operands are read in the
+        // step that uses them instead of one step ahead (holding both spilled, and every spill
+        // reload waited for all the DMA loads in flight). Step kt: wait for stage kt, barrier
+        // (it has landed for every wave, and every wave is past step kt - 1, whose slot is
+        // refilled with stage kt + kRing - 1), read, convert and multiply.
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_vmcnt<(kRing - 2) * kLoads>();
+            __syncthreads();
+            issue(kt + kRing - 1);
+            v8i w0[kNI], a0[kJX];
+            read_ops(kt, w0, a0);
+            mfma32_grid<true>(acc, w0, a0);
+        }
+    } else {
+        v8i w0[kNI], a0[kJX], w1[kNI], a1[kJX];
+        wait_vmcnt<(kRing - 2) * kLoads>();
+        __syncthreads();
+        read_ops(0, w0, a0);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            step(kt, w0, a0, w1, a1);
+            step(kt + 1, w1, a1, w0, a0);
+        }
+        if (kt < nk) step(kt, w0, a0, w1, a1);
     }
-    if (kt < nk) step(kt, w0, a0, w1, a1);
     wait_vmcnt<0>();   // the ring's trailing loads (past k) before the ring is reused
 
     ring_epilogue<TN, TM>(g, acc, m0, n0, ks, smem, t, wn, wm, r32, q);
