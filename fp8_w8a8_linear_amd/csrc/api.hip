@@ -127,8 +127,13 @@ struct MixerWs {
     nhm_ws_layout pub;
     size_t chunk_info, seq_chunk0, chunk_cs, chunk_dt, chunk_state;
     size_t part, part_bytes;   // split-k partials of the projections (prefill)
+    size_t cnt;                // decode: the fused norm's hand-off counters, one per (row, group)
     int max_chunks;
 };
+
+// The decode state kernel computes the gated norm itself (the last of a group's head workgroups
+// takes the group) where a group is at most 512 channels, one pair per thread.
+static bool decode_fused_norm(const nhm_geometry* g) { return (g->n_heads / g->n_groups) * g->head_dim <= 512; }
 
 static MixerWs decode_ws(const nhm_geometry* g, int32_t batch) {
     nhm_layout l;
@@ -145,6 +150,7 @@ static MixerWs decode_ws(const nhm_geometry* g, int32_t batch) {
     w.pub.q_out = take(B * l.d_inner);
     w.part_bytes = batch > 32 ? proj_part_bytes(batch, g->hidden, l.d_inner) : 0;   // out_proj above 32 rows
     w.part = take(w.part_bytes);
+    w.cnt = take(decode_fused_norm(g) ? B * g->n_groups * sizeof(uint32_t) : 0);
     w.pub.total = off;
     return w;
 }
@@ -472,9 +478,17 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
         launch_quantize(hidden, batch, H, H, p->in_proj.a_scale, const_cast<uint8_t*>(q_in), H, st);
         if ((s = check_launch("decode quant")) != NHM_OK) return s;
     }
+    // in_proj on the GEMV, 16 rows a launch; the first launch also zeroes the fused norm's
+    // hand-off counters
+    const bool fused = decode_fused_norm(&p->g);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + w.cnt);
+    if (!use_gemv(16, l.d_in_proj, H))
+        return fail(NHM_ERR_UNSUPPORTED, "decode in_proj %d x %lld outside the GEMV", l.d_in_proj, (long long)H);
     for (int32_t r0 = 0; r0 < batch; r0 += 16) {
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
-        s = project(q_in + (int64_t)r0 * H, H, mg, p->in_proj, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, st);
+        s = launch_gemv(q_in + (int64_t)r0 * H, H, mg, p->in_proj.w, p->in_proj.w_scale, p->in_proj.a_scale,
+                        l.d_in_proj, H, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, st, nullptr, nullptr, 0, nullptr,
+                        fused && r0 == 0 ? cnt : nullptr, fused && r0 == 0 ? batch * p->g.n_groups : 0);
         if (s != NHM_OK) return s;
     }
     DecodeSsmArgs da;
@@ -499,6 +513,15 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
     da.dt_off = l.dt_off;
     da.b_off = l.b_off;
     da.c_off = l.c_off;
+    if (fused) {
+        da.cnt = cnt;
+        da.norm_w = p->norm_w;
+        da.out_a_scale = p->out_proj.a_scale;
+        da.eps = p->g.rms_eps;
+        da.z_off = l.z_off;
+        da.norm = reinterpret_cast<uint16_t*>(wsb + w.pub.norm);
+        da.q_out = q_out;
+    }
     if ((s = launch_decode_ssm(da, batch, st)) != NHM_OK) return s;
     GnormArgs ga{batch, p->g.n_groups, l.d_inner, l.d_in_proj, l.z_off, p->g.rms_eps, da.y, zx, p->norm_w,
                  p->out_proj.a_scale, reinterpret_cast<uint16_t*>(wsb + w.pub.norm), q_out};
@@ -509,7 +532,7 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
     ga.b_off = l.b_off;
     ga.c_off = l.c_off;
     ga.d_state = p->g.d_state;
-    if ((s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
+    if (!fused && (s = launch_gnorm_quant(ga, st)) != NHM_OK) return s;
     // out_proj above 32 rows in one GEMM call (which splits k for these narrow shapes), reading
     // the weight once instead of once per 16 rows: one block at B = 64 104.9 -> 98.0 us; at
     // B = 32 two GEMV launches stay ahead (60.0 against 61.6 us). in_proj stays on the GEMV per

@@ -6,6 +6,17 @@
 // gathered recurrent rows in place). HBM-bound: the state is read and written once
 // (64 KB per workgroup), streamed as 16-byte vectors with every half-wave covering
 // one whole 512-byte state row.
+//
+// Fused gated norm: the heads of a norm group are the group's workgroups of one row, and the
+// last of them to finish also computes the group's gated RMSNorm, the e4m3 codes of its
+// output (the out_proj input) and the shift of the group's B and C conv windows, which every
+// head's workgroup reads. The hand-off uses no fences: each workgroup writes its y through
+// the caches to the device-coherent level (sc0 sc1 stores), waits for those stores, and counts
+// itself in with a relaxed device-scope atomic; the workgroup that counts last reads the
+// group's y past the caches (sc0 sc1 loads). Measured on MI355X in an SSM-update-shaped probe
+// (512 workgroups streaming 32 KB each), this hand-off adds ~2 us per launch against ~16 us
+// for an acquire-release counter, whose fences write back and invalidate each XCD's L2;
+// ~1,000 graph-replayed launches read no stale value.
 #include "nhm_device.h"
 #include "nhm_internal.h"
 
@@ -35,13 +46,29 @@ __device__ __forceinline__ uint32_t conv4_silu(uint32_t bias, uint2 taps, uint32
 // rounded to bf16 (nearest even) on store -- the f32 working row of the f32 pool, narrowed
 // back to the cache dtype at the end of the step.
 template <bool kBf16>
+__device__ __forceinline__ void store_state(v4f* st, v2u* st16, int i, const v4f& v) {
+    if constexpr (kBf16)
+        __builtin_nontemporal_store(v2u{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])}, st16 + i);
+    else
+        __builtin_nontemporal_store(v, st + i);
+}
+
+// The cache policy of the y hand-off: stores written through to, and loads served from, the
+// device-coherent level (sc0 sc1).
+constexpr int kCoherent = 0x11;
+
+template <bool kBf16, bool kFused>
 __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) {
     const int b = blockIdx.x, h = blockIdx.y;
     const int t = threadIdx.x;
     const int hpg = a.n_heads / a.n_groups;
     const int g = h / hpg;
+    const int gw = hpg * kP;              // channels of a norm group (fused: at most 512)
     const int slot = a.slot_idx[b];
     __shared__ float sx[kP], sB[kN], sC[kN];
+    __shared__ uint32_t s_y[kP / 2];
+    __shared__ float s_ss[4];
+    __shared__ uint32_t s_old;
 
     // The small operands first, branch-free (clamped indexes; row b of the workspace exists for
     // a padded row too, and slot row 0 stands in for its window), then the state stream: loads
@@ -60,6 +87,15 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
     uint16_t* win = a.conv_pool + (int64_t)(slot < 0 ? 0 : slot) * 3 * a.conv_dim;
     const uint32_t x0 = win[cx], x1 = win[a.conv_dim + cx], x2 = win[2 * a.conv_dim + cx];
     const uint32_t b0 = win[cb], b1 = win[a.conv_dim + cb], b2 = win[2 * a.conv_dim + cb];
+    // fused: the group's gate values and norm weights, two channels per thread (the workgroup
+    // that finishes the group uses them; loaded by all, ahead of the state stream)
+    uint32_t zz = 0u, nw = 0u;
+    if constexpr (kFused) {
+        if (2 * t < gw) {
+            zz = *reinterpret_cast<const uint32_t*>(a.zxbcdt + (int64_t)b * a.d_in_proj + a.z_off + g * gw + 2 * t);
+            nw = *reinterpret_cast<const uint32_t*>(a.norm_w + g * gw + 2 * t);
+        }
+    }
     asm volatile("" ::: "memory");   // keep the loads above ahead of the state stream
 
     uint16_t* yrow = a.y + (int64_t)b * a.d_inner + h * kP;
@@ -70,7 +106,16 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
             yrow[t] = 0;
             xco[cx] = 0;
         }
-        if (bc_owner) xco[cb] = 0;
+        if (bc_owner) {
+            xco[cb] = 0;
+            if constexpr (kFused) {       // the group's norm output and codes (no hand-off)
+                const int64_t o = (int64_t)b * a.d_inner + g * gw;
+                for (int c = 2 * t; c < gw; c += 512) {
+                    *reinterpret_cast<uint32_t*>(a.norm + o + c) = 0u;
+                    *reinterpret_cast<uint16_t*>(a.q_out + o + c) = 0;
+                }
+            }
+        }
         return;
     }
 
@@ -113,15 +158,12 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
     for (int i = 0; i < 8; ++i) {
         const int p = (t >> 5) + 8 * i;
         const float u = dt * sx[p];
-        v4f v = hv[i];
+        v4f& v = hv[i];
         v[0] = fmaf(dA, v[0], u * b0f);
         v[1] = fmaf(dA, v[1], u * b1f);
         v[2] = fmaf(dA, v[2], u * b2f);
         v[3] = fmaf(dA, v[3], u * b3f);
-        if constexpr (kBf16)
-            __builtin_nontemporal_store(v2u{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])}, st16 + t + 256 * i);
-        else
-            __builtin_nontemporal_store(v, st + t + 256 * i);
+        if constexpr (!kFused) store_state<kBf16>(st, st16, t + 256 * i, v);
         yp[i] = v[0] * c0 + v[1] * c1 + v[2] * c2 + v[3] * c3;
     }
     // reduce over the 32 lanes that share p
@@ -130,20 +172,78 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
 #pragma unroll
         for (int o = 16; o >= 1; o >>= 1) yp[i] += __shfl_xor(yp[i], o, kWave);
     }
-    if ((t & 31) == 0) {
+    if constexpr (!kFused) {
+        if ((t & 31) == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int p = (t >> 5) + 8 * i;
-            yrow[p] = (uint16_t)f32_to_bf16(yp[i] + Dh * sx[p]);
+            for (int i = 0; i < 8; ++i) {
+                const int p = (t >> 5) + 8 * i;
+                yrow[p] = (uint16_t)f32_to_bf16(yp[i] + Dh * sx[p]);
+            }
         }
+        return;
+    } else {
+        if ((t & 31) == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int p = (t >> 5) + 8 * i;
+                reinterpret_cast<uint16_t*>(s_y)[p] = (uint16_t)f32_to_bf16(yp[i] + Dh * sx[p]);
+            }
+        }
+        __syncthreads();
+        // y written through to the device-coherent level and waited for, then counted in; the
+        // state stores go out behind the count, while its round trip is in flight
+        const __amdgpu_buffer_rsrc_t yrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((int64_t)gridDim.x * a.d_inner * 2), 0x00020000);
+        if (t < kP / 2) __builtin_amdgcn_raw_buffer_store_b32(s_y[t], yrs, (uint32_t)(((int64_t)b * a.d_inner + h * kP + 2 * t) * 2), 0, kCoherent);
+        wait_vmcnt<0>();
+        __syncthreads();
+        uint32_t old = 0u;
+        if (t == 0) old = __hip_atomic_fetch_add(a.cnt + (int64_t)b * a.n_groups + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 8; ++i) store_state<kBf16>(st, st16, t + 256 * i, hv[i]);
+        if (t == 0) s_old = old;
+        __syncthreads();
+        if (s_old % (uint32_t)hpg != (uint32_t)(hpg - 1)) return;
+
+        // Last of the group: gated RMSNorm over the group's gw channels (two per thread), the
+        // codes E4M3(o / s_out) of the bf16 output, and the shift of the group's B and C windows
+        // (thread t holds channel cb's window rows and current value).
+        const int64_t o = (int64_t)b * a.d_inner + g * gw;
+        float v0 = 0.f, v1 = 0.f, ss = 0.f;
+        if (2 * t < gw) {
+            const uint32_t yy = __builtin_amdgcn_raw_buffer_load_b32(yrs, (uint32_t)((o + 2 * t) * 2), 0, kCoherent);
+            v0 = bf16_to_f32(yy & 0xffffu) * silu(bf16_to_f32(zz & 0xffffu));
+            v1 = bf16_to_f32(yy >> 16) * silu(bf16_to_f32(zz >> 16));
+            ss = v0 * v0 + v1 * v1;
+        }
+        ss = wave_sum(ss);
+        if ((t & 63) == 0) s_ss[t >> 6] = ss;
+        __syncthreads();
+        ss = s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3];
+        const float r = 1.0f / sqrtf(ss / (float)gw + a.eps);
+        if (2 * t < gw) {
+            const uint32_t ob = f32x2_to_bf16x2(v0 * r * bf16_to_f32(nw & 0xffffu), v1 * r * bf16_to_f32(nw >> 16));
+            *reinterpret_cast<uint32_t*>(a.norm + o + 2 * t) = ob;
+            const float so = *a.out_a_scale;
+            *reinterpret_cast<uint16_t*>(a.q_out + o + 2 * t) =
+                (uint16_t)(quant_bf16(ob & 0xffffu, so) | (quant_bf16(ob >> 16, so) << 8));
+        }
+        win[cb] = (uint16_t)b1;
+        win[a.conv_dim + cb] = (uint16_t)b2;
+        win[2 * a.conv_dim + cb] = (uint16_t)bcur;
     }
 }
 
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st) {
-    if (a.ssm_pool_bf16)
-        decode_ssm_kernel<true><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
-    else
-        decode_ssm_kernel<false><<<dim3(m, a.n_heads), dim3(256), 0, st>>>(a);
+    const dim3 grid(m, a.n_heads);
+    if (a.cnt) {
+        if (a.ssm_pool_bf16) decode_ssm_kernel<true, true><<<grid, dim3(256), 0, st>>>(a);
+        else decode_ssm_kernel<false, true><<<grid, dim3(256), 0, st>>>(a);
+    } else {
+        if (a.ssm_pool_bf16) decode_ssm_kernel<true, false><<<grid, dim3(256), 0, st>>>(a);
+        else decode_ssm_kernel<false, false><<<grid, dim3(256), 0, st>>>(a);
+    }
     count_launch(Kern::kDecodeSsm, m);
     return check_launch("decode_ssm");
 }

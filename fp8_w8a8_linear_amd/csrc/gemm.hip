@@ -443,12 +443,6 @@ __device__ __forceinline__ void dma16(const i32x4& rs, const uint8_t* lds, uint3
                  : "memory", "m0");
 }
 
-// s_waitcnt with vmcnt <= n (n < 64), expcnt and lgkmcnt left alone
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Block -> (tile origin m0, n0; k split ks) of a ring kernel. Blocks go to the 8 XCDs round

@@ -29,6 +29,7 @@ struct GemvArgs {
     // at out_q[m * ld_q + n] -- the next projection's pre-quantized input
     uint8_t* out_q; int64_t ld_q; const float* q_scale; bool vec_q;
     int ksteps;
+    uint32_t* clear; int clear_n;                   // words zeroed by workgroup 0 (side work)
     // workgroup b owns features [b base + min(b, extra), ...) -- base + 1 of them for b < extra,
     // base for the others (at most 16 x kTiles)
     int base, extra;
@@ -44,6 +45,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves - 1][kTiles][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
+    if (b == 0 && g.clear) {
+        for (int i = threadIdx.x; i < g.clear_n; i += kWaves * 64) g.clear[i] = 0u;
+    }
     const int64_t n0 = (int64_t)b * g.base + (b < g.extra ? b : g.extra);
     const int64_t nend = n0 + g.base + (b < g.extra ? 1 : 0);   // this workgroup's features end
     const int col = lane & 15;                  // B operand column (token)
@@ -163,8 +167,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
-                       float* out_f32, uint8_t* out_q, int64_t ld_q, const float* q_scale) {
+                       float* out_f32, uint8_t* out_q, int64_t ld_q, const float* q_scale, uint32_t* clear,
+                       int clear_n) {
     GemvArgs g;
+    g.clear = clear_n > 0 ? clear : nullptr;
+    g.clear_n = clear_n;
     g.out_q = out_f32 ? nullptr : out_q;
     g.ld_q = ld_q;
     g.q_scale = q_scale;

@@ -176,4 +176,10 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// s_waitcnt with vmcnt <= n (n < 64), expcnt and lgkmcnt left alone
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
 }  // namespace nhm

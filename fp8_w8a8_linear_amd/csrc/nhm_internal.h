@@ -40,10 +40,11 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
 // out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda], stored to
 // out[m * ld_out + n]; with out_f32 the unrounded f32 result goes to out_f32[m * ld_out + n]
 // instead. out_q (bf16 output only): also E4M3(out / *q_scale) at out_q[m * ld_q + n].
+// clear (optional): clear_n 32-bit words set to zero by the launch (side work of workgroup 0)
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
                        float* out_f32 = nullptr, uint8_t* out_q = nullptr, int64_t ld_q = 0,
-                       const float* q_scale = nullptr);
+                       const float* q_scale = nullptr, uint32_t* clear = nullptr, int clear_n = 0);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 // part (16-byte aligned, part_bytes >= gemm_part_bytes(m, n, k)): scratch for the split-k
@@ -76,6 +77,16 @@ struct DecodeSsmArgs {
     const float* dt_bias;
     uint16_t* y;               // [m, d_inner]
     int32_t n_heads, n_groups, d_in_proj, conv_dim, d_inner, xbc_off, dt_off, b_off, c_off;
+    // fused gated norm (cnt != nullptr): the last of a group's head workgroups to finish also
+    // computes the group's gated RMSNorm and its e4m3 codes and shifts the group's B and C conv
+    // windows; cnt holds one counter per (row, group), zero at launch
+    uint32_t* cnt = nullptr;
+    const uint16_t* norm_w = nullptr;   // [d_inner]
+    const float* out_a_scale = nullptr;
+    float eps = 0.f;
+    int32_t z_off = 0;
+    uint16_t* norm = nullptr;           // [m, d_inner]
+    uint8_t* q_out = nullptr;           // [m, d_inner]
 };
 nhm_status launch_decode_ssm(const DecodeSsmArgs& a, int m, hipStream_t st);
 

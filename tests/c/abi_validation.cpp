@@ -23,7 +23,7 @@ void launch_dequant_channel(const uint8_t*, int64_t, int64_t, int64_t, const flo
     reached("launch_dequant_channel");
 }
 nhm_status launch_gemv(const uint8_t*, int64_t, int, const uint8_t*, const float*, const float*, int64_t, int64_t,
-                       uint16_t*, int64_t, hipStream_t, float*, uint8_t*, int64_t, const float*) {
+                       uint16_t*, int64_t, hipStream_t, float*, uint8_t*, int64_t, const float*, uint32_t*, int) {
     reached("launch_gemv");
 }
 // The workspace queries size the split-k partials with this; the driver checks only that

@@ -275,3 +275,41 @@ def test_linear_exact(nhm, m, n, k):
     # the bf16 output is the f32 output rounded once
     assert np.array_equal(of.to(torch.bfloat16).view(torch.int16).cpu().numpy(), host(ob).view(np.int16))
     print(f"exact {m}x{n}x{k}: max |d| / (2^-24 S) = {np.max(np.abs(of.cpu().numpy() - ref) / (2.0 ** -24 * S)):.3f}")
+
+
+# The GEMV on the decode shapes (in_proj 10304 x 2688, out_proj 2688 x 4096) at every row count
+# class it serves, against the oracle as test_linear_exact bounds it: the activation codes given
+# at a row stride past k whose extra bytes hold large codes (e4m3 input through the raw ABI), and
+# as bf16 (quantized by the library); both calls agree bit for bit, and the dispatch counters
+# show the GEMV ran.
+@pytest.mark.parametrize("m", [1, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("n,k", [(10304, 2688), (2688, 4096)])
+def test_gemv_decode_shapes(nhm, m, n, k):
+    import ctypes as C
+    from oracle import bf16_to_f64, e4m3_decode, fp8_linear, quantize_static
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=14)
+    q = quantize_static(a, sa)
+    ref = fp8_linear(q, w, ws, sa)
+    S = np.abs(e4m3_decode(q)) @ np.abs(e4m3_decode(w)).T * np.float64(sa[0]) * ws.astype(np.float64)[None, :]
+    W = nhm.Fp8Weight(dev(w), dev(ws), dev(sa))
+    lda = k + 48
+    qs = np.full((m, lda), 0x7E, dtype=np.uint8)            # past-k bytes hold large codes
+    qs[:, :k] = q
+    qd = dev(qs)
+    out = torch.zeros((m, n), dtype=torch.int16, device="cuda")
+    nhm.dispatch_counters(reset=True)
+    st = nhm.lib.nhm_fp8_linear_exact(C.c_void_p(qd.data_ptr()), nhm.NHM_E4M3, m, lda, C.byref(W.struct),
+                                      C.c_void_p(out.data_ptr()), nhm.NHM_BF16, n, None, 0,
+                                      C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, nhm.lib.nhm_last_error()
+    ob2 = nhm.fp8_linear(dev(a), W, exact=True)
+    torch.cuda.synchronize()
+    assert nhm.dispatch_counters(reset=True) == {"gemv": (2, 2 * m), "quant_vec8": (1, m)}
+    for got in (bf16_to_f64(host(out)), bf16_to_f64(host(ob2))):
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -22 * S
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert np.all(err <= bound), f"at {worst}: got {got[worst]} ref {ref[worst]} bound {bound[worst]}"
+    assert np.array_equal(host(out), host(ob2))
