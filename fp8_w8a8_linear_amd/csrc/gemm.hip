@@ -688,11 +688,6 @@ __global__ __launch_bounds__(512) void tile256_kernel(const GemmArgs g) {
     ring_epilogue<TN, TM>(g, acc, m0, n0, ks, smem, t, wn, wm, r32, q);
 }
 
-// 128-byte LDS rows: chunk c of row r sits at slot c ^ (r & 7) ^ ((r >> 3) & 1). A b128 read
-// serves 16 lanes per pass; 16 consecutive rows read at one chunk land on 16 distinct 16-byte
-// units of the 256-byte bank window (rows of one parity differ in the slot's low bits, the two
-// parities sit 64 bytes apart, and bit 3 of the row flips the slot's lowest bit).
-__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7) ^ ((row >> 3) & 1)) << 4); }
 
 // The ring tile kernel with 128-byte k-stages: a stage holds 128 bytes of k for each of the
 // TN + TM rows, so every DMA request is a whole 128-byte line (the 64-byte stages issue half

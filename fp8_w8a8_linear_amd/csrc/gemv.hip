@@ -6,6 +6,16 @@
 // the B operand; the e4m3 codes are converted to bf16 in registers (exact) and summed
 // by the bf16 MFMA, which accumulates in full f32.
 //
+// Weight loads. In the 8-wave configuration (one row tile per workgroup, 2944 <= k <= 8192:
+// out_proj among them), each load instruction brings whole 128-byte lines -- 8 weight rows x 128
+// bytes of one k-step -- and every k-step passes through a per-wave LDS buffer to reach the
+// MFMA's operand layout (row = lane % 16). Otherwise (in_proj's three tiles; the 16-wave
+// configurations, whose 128-register budget the buffer's traffic would overflow) each
+// instruction brings 16 rows x 64 bytes straight into the operand registers. Measured on MI355X at m = 8:
+// out_proj 2688 x 4096 5.26 -> 4.58 us with whole lines; in_proj 10304 x 2688 8.48 us straight,
+// 9.1-9.4 us with whole lines and the transpose (its extra LDS round trips per step do not
+// hide behind one wave per SIMD), both bit-identical.
+//
 // Decomposition: one workgroup owns up to 48 output features (one to three 16-row MFMA
 // tiles, as many as keep the busiest CU's operand bytes lowest) and the whole k range; its
 // waves take the 128-wide k-steps round-robin (neighbouring waves read neighbouring
@@ -40,9 +50,11 @@ struct GemvArgs {
 // either 9.23), although each weight row is read once per call.
 constexpr int kStreamAux = 0;
 
-template <int kWaves, int kSteps, int kTiles>
+template <int kWaves, int kSteps, int kTiles, bool kLines>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     __shared__ v4f s_red[kWaves - 1][kTiles][64];
+    // kLines: this wave's transpose buffer, one k-step of the 16 kTiles rows
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[kLines ? kWaves : 1][kLines ? 16 * kTiles * 128 : 16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
     if (b == 0 && g.clear) {
@@ -80,15 +92,35 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         wrow[t] = row < nend ? (uint32_t)(row * g.k) : kGemvOut;
     }
     const uint32_t arow = col < g.m ? (uint32_t)(col * g.lda) : kGemvOut;
+    // kLines: unit u of a tile's k-step is rows 8u .. 8u + 7 of the tile, lane l on row 8u + l / 8,
+    // loading the 16-byte chunk that swz128 places at slot l % 8 of that row
+    const int lr = lane >> 3, slot = lane & 7;
+    uint32_t urow[2 * kTiles];
+    int uch[2 * kTiles];
+    if constexpr (kLines) {
+#pragma unroll
+        for (int u = 0; u < 2 * kTiles; ++u) {
+            const int r8 = 8 * u + lr;
+            urow[u] = n0 + r8 < nend ? (uint32_t)((n0 + r8) * g.k) : kGemvOut;
+            uch[u] = 16 * (slot ^ (r8 & 7) ^ ((r8 >> 3) & 1));
+        }
+    }
     // weight and activation pieces of each k-step are issued together
     v8i wa[kSteps][kTiles], xb[kSteps];
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
         const int kb = (wave + i * kWaves) * 128 + kq;
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t)
-            wa[i][t] = bload32<kStreamAux>(wrs, kb < g.k ? wrow[t] + kb : kGemvOut,
-                                           kb + 16 < g.k ? wrow[t] + kb + 16 : kGemvOut);
+        for (int t = 0; t < kTiles; ++t) {
+            if constexpr (kLines) {
+                const int k0 = kb - kq + uch[2 * t], k1 = kb - kq + uch[2 * t + 1];
+                wa[i][t] = bload32<kStreamAux>(wrs, k0 < g.k ? urow[2 * t] + k0 : kGemvOut,
+                                               k1 < g.k ? urow[2 * t + 1] + k1 : kGemvOut);
+            } else {
+                wa[i][t] = bload32<kStreamAux>(wrs, kb < g.k ? wrow[t] + kb : kGemvOut,
+                                               kb + 16 < g.k ? wrow[t] + kb + 16 : kGemvOut);
+            }
+        }
         xb[i] = bload32<0>(ars, kb < g.k ? arow + kb : kGemvOut, kb + 16 < g.k ? arow + kb + 16 : kGemvOut);
     }
     // keep every load above issued before the first MFMA (the scheduler would otherwise sink
@@ -105,7 +137,23 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i)
+    for (int i = 0; i < kSteps; ++i) {
+        if constexpr (kLines) {   // step i's rows, written as loaded, read back in operand layout
+            uint8_t* const tb = s_tr[wave];
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) {
+                *reinterpret_cast<uint4*>(tb + (16 * t + lr) * 128 + slot * 16) =
+                    make_uint4(wa[i][t][0], wa[i][t][1], wa[i][t][2], wa[i][t][3]);
+                *reinterpret_cast<uint4*>(tb + (16 * t + 8 + lr) * 128 + slot * 16) =
+                    make_uint4(wa[i][t][4], wa[i][t][5], wa[i][t][6], wa[i][t][7]);
+            }
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) {
+                const uint4 w0 = *reinterpret_cast<const uint4*>(tb + swz128(16 * t + col, 2 * (lane >> 4)));
+                const uint4 w1 = *reinterpret_cast<const uint4*>(tb + swz128(16 * t + col, 2 * (lane >> 4) + 1));
+                wa[i][t] = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bf16x8 xs = e4m3x8_to_bf16(xb[i][2 * j], xb[i][2 * j + 1]);
@@ -113,6 +161,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
             for (int t = 0; t < kTiles; ++t)
                 acc[t] = mfma_bf16(e4m3x8_to_bf16(wa[i][t][2 * j], wa[i][t][2 * j + 1]), xs, acc[t]);
         }
+    }
 
     if (wave > 0) {
 #pragma unroll
@@ -207,7 +256,7 @@ nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, c
     g.extra = (int)(n % wgs);
     const int tiles = (g.base + (g.extra ? 1 : 0) + 15) / 16;
     const dim3 grid((unsigned)wgs);
-#define NHM_GEMV_LAUNCH(W, S, T) gemv_kernel<W, S, T><<<grid, dim3(W * 64), 0, st>>>(g)
+#define NHM_GEMV_LAUNCH(W, S, T) gemv_kernel<W, S, T, (W == 8)><<<grid, dim3(W * 64), 0, st>>>(g)
 #define NHM_GEMV_STEPS(W, T)                         \
     do {                                             \
         if (steps == 2) NHM_GEMV_LAUNCH(W, 2, T);    \

@@ -182,4 +182,10 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// 128-byte LDS rows: chunk c of row r sits at slot c ^ (r & 7) ^ ((r >> 3) & 1). A b128 read
+// serves 16 lanes per pass; 16 consecutive rows read at one chunk land on 16 distinct 16-byte
+// units of the 256-byte bank window (rows of one parity differ in the slot's low bits, the two
+// parities sit 64 bytes apart, and bit 3 of the row flips the slot's lowest bit).
+__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7) ^ ((row >> 3) & 1)) << 4); }
+
 }  // namespace nhm
