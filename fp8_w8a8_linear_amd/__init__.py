@@ -54,7 +54,7 @@ class _DispatchCounter(C.Structure):
 
 class _Fp8Weight(C.Structure):
     _fields_ = [("w", C.c_void_p), ("w_scale", C.c_void_p), ("a_scale", C.c_void_p), ("n", C.c_int64),
-                ("k", C.c_int64)]
+                ("k", C.c_int64), ("w_scale_per_tensor", C.c_int32)]
 
 
 class _MixerParams(C.Structure):
@@ -133,14 +133,20 @@ def _dev_tensor(x, name):
 
 
 class Fp8Weight:
-    """One FP8 W8A8 projection on the device: e4m3 codes [n, k] (uint8), f32 scale [n], f32 a_scale [1]."""
+    """One FP8 W8A8 projection on the device: e4m3 codes [n, k] (uint8), f32 weight scale [n] (per
+    output channel) or [1] (per tensor), f32 a_scale [1]."""
 
     def __init__(self, w, w_scale, a_scale):
         self.w = _dev_tensor(w, "w")
         self.w_scale = _dev_tensor(w_scale, "w_scale")
         self.a_scale = _dev_tensor(a_scale, "a_scale")
         self.n, self.k = int(w.shape[0]), int(w.shape[1])
-        self._s = _Fp8Weight(self.w.data_ptr(), self.w_scale.data_ptr(), self.a_scale.data_ptr(), self.n, self.k)
+        ns = int(self.w_scale.numel())
+        if ns not in (1, self.n):
+            raise ValueError(f"w_scale has {ns} entries: {self.n} (per channel) or 1 (per tensor)")
+        self.per_tensor = ns == 1 and self.n != 1
+        self._s = _Fp8Weight(self.w.data_ptr(), self.w_scale.data_ptr(), self.a_scale.data_ptr(), self.n, self.k,
+                             1 if self.per_tensor else 0)
 
     @property
     def struct(self):

@@ -92,8 +92,14 @@ static nhm_status check_weight(const nhm_fp8_weight* w, int64_t n, int64_t k, co
                     (long long)w->n, (long long)w->k, (long long)n, (long long)k);
     if (!aligned(w->w, 16) || !aligned(w->w_scale, 4) || !aligned(w->a_scale, 4))
         return fail(NHM_ERR_ALIGN, "%s: weight must be 16-byte aligned, scales 4-byte aligned", name);
+    if (w->w_scale_per_tensor != 0 && w->w_scale_per_tensor != 1)
+        return fail(NHM_ERR_UNSUPPORTED, "%s: w_scale_per_tensor %d: 0 (per channel) or 1 (per tensor)", name,
+                    (int)w->w_scale_per_tensor);
     return NHM_OK;
 }
+
+// Index step of the weight scale: per channel (w_scale[n]) or one scale for every channel.
+static int ws_step(const nhm_fp8_weight& w) { return w.w_scale_per_tensor ? 0 : 1; }
 
 // ---------------------------------------------------------------- workspace layouts
 
@@ -193,9 +199,9 @@ static nhm_status project(const uint8_t* a, int64_t lda, int64_t m, const nhm_fp
                           const float* q_scale = nullptr) {
     if (use_gemv(m, w.n, w.k))
         return launch_gemv(a, lda, (int)m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, out_q, ld_q,
-                           q_scale);
+                           q_scale, nullptr, 0, ws_step(w));
     return launch_gemm(a, lda, m, w.w, w.w_scale, w.a_scale, w.n, w.k, out, ld_out, st, out_f32, part, part_bytes,
-                       exact);
+                       exact, ws_step(w));
 }
 
 static nhm_status check_params(const nhm_mixer_params* p, nhm_layout* l) {
@@ -488,7 +494,8 @@ static nhm_status decode_call(const nhm_mixer_params* p, const uint16_t* hidden,
         const int mg = batch - r0 < 16 ? batch - r0 : 16;
         s = launch_gemv(q_in + (int64_t)r0 * H, H, mg, p->in_proj.w, p->in_proj.w_scale, p->in_proj.a_scale,
                         l.d_in_proj, H, zx + (int64_t)r0 * l.d_in_proj, l.d_in_proj, st, nullptr, nullptr, 0, nullptr,
-                        fused && r0 == 0 ? cnt : nullptr, fused && r0 == 0 ? batch * p->g.n_groups : 0);
+                        fused && r0 == 0 ? cnt : nullptr, fused && r0 == 0 ? batch * p->g.n_groups : 0,
+                        ws_step(p->in_proj));
         if (s != NHM_OK) return s;
     }
     DecodeSsmArgs da;

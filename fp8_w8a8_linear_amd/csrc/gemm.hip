@@ -47,6 +47,7 @@ struct GemmArgs {
     // adds up in split order, scales and rounds
     int ksplit = 1;
     float* part = nullptr;
+    int ws_step = 1;    // weight scale index step: 1 per channel, 0 per tensor
 };
 
 // Row r of a 128-byte-wide LDS tile holds its 16-byte chunk c at slot c ^ (r & 7):
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t c = nw0 + i * 16 + 4 * q + r;
-            wsc[i][r] = g.w_scale[c < g.n ? c : g.n - 1];
+            wsc[i][r] = g.w_scale[(c < g.n ? c : g.n - 1) * g.ws_step];
         }
     }
     uint32_t aoff[LA];
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t c = n0 + wn * 64 + i * 16 + 4 * q + r;
-            wsc[i][r] = g.w_scale[c < g.n ? c : g.n - 1];
+            wsc[i][r] = g.w_scale[(c < g.n ? c : g.n - 1) * g.ws_step];
         }
 
     v4f acc[4][4];
@@ -506,7 +507,7 @@ __device__ __forceinline__ void ring_epilogue(const GemmArgs& g, v16f (&acc)[TN 
                 const int64_t nb = n0 + wn * (TN / 2) + i * 32 + gq * 8 + q * 4;
                 float sc[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
+                for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[(nb + r < g.n ? nb + r : g.n - 1) * g.ws_step];
 #pragma unroll
                 for (int jx = 0; jx < kJX; ++jx) {
                     const int64_t mm = m0 + wm * (TM / 4) + jx * 32 + r32;
@@ -525,7 +526,7 @@ __device__ __forceinline__ void ring_epilogue(const GemmArgs& g, v16f (&acc)[TN 
             const int64_t nb = n0 + nl + q * 4;
             float sc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[nb + r < g.n ? nb + r : g.n - 1];
+            for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[(nb + r < g.n ? nb + r : g.n - 1) * g.ws_step];
 #pragma unroll
             for (int jx = 0; jx < kJX; ++jx) {
                 const int ml = wm * (TM / 4) + jx * 32 + r32;
@@ -813,7 +814,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
         const int64_t mm = e0 / g.n, nn = e0 - mm * g.n;
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = v[r] * (sa * g.w_scale[nn + r]);
+        for (int r = 0; r < 4; ++r) o[r] = v[r] * (sa * g.w_scale[(nn + r) * g.ws_step]);
         if (g.out_f32) {
             float* d = g.out_f32 + mm * g.ld_out + nn;
             if (g.vec_out) {
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
         const int64_t e = e0 + r, mm = e / g.n, nn = e - mm * g.n;
         float acc = 0.f;
         for (int s = 0; s < g.ksplit; ++s) acc += g.part[(int64_t)s * mn + e];
-        const float o = acc * (sa * g.w_scale[nn]);
+        const float o = acc * (sa * g.w_scale[nn * g.ws_step]);
         if (g.out_f32) g.out_f32[mm * g.ld_out + nn] = o;
         else g.out[mm * g.ld_out + nn] = (uint16_t)f32_to_bf16(o);
     }
@@ -952,11 +953,12 @@ static nhm_status dispatch_gemm(GemmArgs g, hipStream_t st, float* part, size_t 
 
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
-                       hipStream_t st, float* out_f32, float* part, size_t part_bytes, bool exact) {
+                       hipStream_t st, float* out_f32, float* part, size_t part_bytes, bool exact, int ws_step) {
     GemmArgs g{a, lda, m, w, w_scale, a_scale, n, k, out, ld_out,
                out_f32 ? ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out_f32) % 16 == 0
                        : ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0,
                out_f32};
+    g.ws_step = ws_step;
     return exact ? dispatch_gemm<true>(g, st, part, part_bytes) : dispatch_gemm<false>(g, st, part, part_bytes);
 }
 

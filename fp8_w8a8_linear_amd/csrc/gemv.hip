@@ -40,6 +40,7 @@ struct GemvArgs {
     uint8_t* out_q; int64_t ld_q; const float* q_scale; bool vec_q;
     int ksteps;
     uint32_t* clear; int clear_n;                   // words zeroed by workgroup 0 (side work)
+    int ws_step;                                    // weight scale index step: 1 per channel, 0 per tensor
     // workgroup b owns features [b base + min(b, extra), ...) -- base + 1 of them for b < extra,
     // base for the others (at most 16 x kTiles)
     int base, extra;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[nbase[t] + r < g.n ? nbase[t] + r : g.n - 1];
+        for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[(nbase[t] + r < g.n ? nbase[t] + r : g.n - 1) * g.ws_step];
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
@@ -217,8 +218,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
                        float* out_f32, uint8_t* out_q, int64_t ld_q, const float* q_scale, uint32_t* clear,
-                       int clear_n) {
+                       int clear_n, int ws_step) {
     GemvArgs g;
+    g.ws_step = ws_step;
     g.clear = clear_n > 0 ? clear : nullptr;
     g.clear_n = clear_n;
     g.out_q = out_f32 ? nullptr : out_q;

@@ -40,11 +40,12 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
 // out[m, n] = bf16(sum_k a[m,k] w[n,k] * a_scale * w_scale[n]); a is e4m3 [m, lda], stored to
 // out[m * ld_out + n]; with out_f32 the unrounded f32 result goes to out_f32[m * ld_out + n]
 // instead. out_q (bf16 output only): also E4M3(out / *q_scale) at out_q[m * ld_q + n].
-// clear (optional): clear_n 32-bit words set to zero by the launch (side work of workgroup 0)
+// clear (optional): clear_n 32-bit words set to zero by the launch (side work of workgroup 0).
+// ws_step: 1 for a weight scale per output channel, 0 for one scale (w_scale[0]) for all.
 nhm_status launch_gemv(const uint8_t* a, int64_t lda, int m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out, hipStream_t st,
                        float* out_f32 = nullptr, uint8_t* out_q = nullptr, int64_t ld_q = 0,
-                       const float* q_scale = nullptr, uint32_t* clear = nullptr, int clear_n = 0);
+                       const float* q_scale = nullptr, uint32_t* clear = nullptr, int clear_n = 0, int ws_step = 1);
 
 // ---- tiled MFMA GEMM for larger m (gemm.hip)
 // part (16-byte aligned, part_bytes >= gemm_part_bytes(m, n, k)): scratch for the split-k
@@ -56,7 +57,7 @@ size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
 nhm_status launch_gemm(const uint8_t* a, int64_t lda, int64_t m, const uint8_t* w, const float* w_scale,
                        const float* a_scale, int64_t n, int64_t k, uint16_t* out, int64_t ld_out,
                        hipStream_t st, float* out_f32 = nullptr, float* part = nullptr, size_t part_bytes = 0,
-                       bool exact = false);
+                       bool exact = false, int ws_step = 1);
 
 // ---- decode SSM state update (decode.hip)
 // The kernel also runs the causal conv + SiLU of the channels it reads (the head's x, the

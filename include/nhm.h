@@ -142,14 +142,20 @@ NHM_API nhm_status nhm_mixer_layout(const nhm_geometry* g, nhm_layout* out);
 
 /* One FP8 W8A8 projection: e4m3 weight in the [out, in] torch-Linear orientation
  * (row-major [n, k]; [PR950] "Review repairs" F2: the GEMM consumers refuse any
- * other orientation), an f32 scale per output channel, and the static per-tensor
- * f32 activation scale ("input_scale"). All three pointers are device memory. */
+ * other orientation), its f32 weight scale, and the static per-tensor f32 activation
+ * scale ("input_scale"). All three pointers are device memory. The weight scale is one
+ * f32 per output channel, or, with w_scale_per_tensor = 1, one f32 for the whole
+ * projection: the form the checkpoint carries, two f32 scalars per FP8 projection
+ * ([PR950] "Review repairs" F2, weight_scale beside input_scale). A zero-initialised
+ * field keeps the per-channel form. */
 typedef struct nhm_fp8_weight {
     const uint8_t* w;         /* (device) e4m3 [n, k], row stride k, 16-B aligned */
-    const float* w_scale;     /* (device) f32 [n]                                 */
+    const float* w_scale;     /* (device) f32 [n], or f32 [1] when per tensor     */
     const float* a_scale;     /* (device) f32 [1]                                 */
     int64_t n;                /* output features                                  */
     int64_t k;                /* input features, k % 16 == 0                      */
+    int32_t w_scale_per_tensor; /* 0: per output channel; 1: one scale; other values
+                                   are refused (NHM_ERR_UNSUPPORTED)                */
 } nhm_fp8_weight;
 
 /* Static per-tensor activation quant: q[r, c] = E4M3(f32(x[r, c]) / scale[0]),

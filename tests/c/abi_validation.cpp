@@ -23,14 +23,14 @@ void launch_dequant_channel(const uint8_t*, int64_t, int64_t, int64_t, const flo
     reached("launch_dequant_channel");
 }
 nhm_status launch_gemv(const uint8_t*, int64_t, int, const uint8_t*, const float*, const float*, int64_t, int64_t,
-                       uint16_t*, int64_t, hipStream_t, float*, uint8_t*, int64_t, const float*, uint32_t*, int) {
+                       uint16_t*, int64_t, hipStream_t, float*, uint8_t*, int64_t, const float*, uint32_t*, int, int) {
     reached("launch_gemv");
 }
 // The workspace queries size the split-k partials with this; the driver checks only that
 // they succeed, so the stub reports none.
 size_t gemm_part_bytes(int64_t, int64_t, int64_t) { return 0; }
 nhm_status launch_gemm(const uint8_t*, int64_t, int64_t, const uint8_t*, const float*, const float*, int64_t, int64_t,
-                       uint16_t*, int64_t, hipStream_t, float*, float*, size_t, bool) {
+                       uint16_t*, int64_t, hipStream_t, float*, float*, size_t, bool, int) {
     reached("launch_gemm");
 }
 nhm_status launch_decode_ssm(const DecodeSsmArgs&, int, hipStream_t) { reached("launch_decode_ssm"); }

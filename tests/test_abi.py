@@ -74,8 +74,8 @@ def test_n_heads_not_multiple_of_8_refused(nhm):
     assert nhm.mixer_layout(dict(nhm.GEOMETRY, n_heads=8, n_groups=2, hidden=256))["d_in_proj"] % 8 == 0
 
 
-def _w(nhm, w=0x1000, s=0x2000, a=0x3000, n=64, k=128):
-    return nhm._Fp8Weight(w, s, a, n, k)
+def _w(nhm, w=0x1000, s=0x2000, a=0x3000, n=64, k=128, per_tensor=0):
+    return nhm._Fp8Weight(w, s, a, n, k, per_tensor)
 
 
 def _lin(nhm, a, a_type, m, lda, w, out, ld_out, ws, wsb):
@@ -91,6 +91,7 @@ def test_linear_refusals(nhm):
         (dict(w=_w(nhm, k=100)), 2), (dict(w=_w(nhm, n=0)), 2), (dict(m=-1), 2), (dict(lda=64), 2),
         (dict(ld_out=10), 2), (dict(a=A + 2), 3), (dict(w=_w(nhm, w=0x1008)), 3), (dict(out=O + 1), 3),
         (dict(wsb=need - 1), 5), (dict(ws=None), 5), (dict(a_type=7), 4), (dict(ws=WS + 8), 3),
+        (dict(w=_w(nhm, per_tensor=2)), 4), (dict(w=_w(nhm, per_tensor=-1)), 4),
     ]
     for over, status in cases:
         kw = dict(a=A, a_type=nhm.NHM_BF16, m=32, lda=128, w=_w(nhm), out=O, ld_out=64, ws=WS, wsb=need)

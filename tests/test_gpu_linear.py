@@ -101,6 +101,27 @@ def test_linear_per_tensor_weight_scale(nhm, m, n, k):
     _check(nhm, a, w, ws, sa)
 
 
+# The per-tensor form the checkpoint carries (w_scale_per_tensor = 1, one f32) against the same
+# scale broadcast to a per-channel vector: bit-identical on every dispatch path -- the GEMV at
+# both row classes, the 64 x 128 panel, the 192 x 128 ring, the split-k ring with its
+# reduction, the 256 x 256 tile -- with bf16 and f32 output and with exact sums.
+@pytest.mark.parametrize("m,n,k", [(1, 10304, 2688), (8, 2688, 4096), (200, 10304, 2688), (512, 10304, 2688),
+                                   (64, 4096, 4096), (33, 1002, 4096), (2600, 4100, 272)])
+def test_linear_per_tensor_scale_form(nhm, m, n, k):
+    from tests.gpu_util import dev, host
+    from workloads import linear_case
+    a, w, ws, sa = linear_case(m, n, k, extra=11, per_tensor=True)
+    wd, ad, sad = dev(w), dev(a), dev(sa)
+    vec = nhm.Fp8Weight(wd, dev(ws), sad)
+    one = nhm.Fp8Weight(wd, dev(ws[:1].copy()), sad)
+    assert one.per_tensor and not vec.per_tensor
+    for kw in (dict(), dict(out_type=nhm.NHM_F32), dict(exact=True)):
+        ov = nhm.fp8_linear(ad, vec, **kw)
+        o1 = nhm.fp8_linear(ad, one, **kw)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ov), host(o1)), kw
+
+
 # Narrow shapes whose panel launch would leave most of the chip idle: with the workspace the
 # query reports, the 192 x 128 ring tile over S k ranges plus the reduction (33 x 1002: ragged
 # m and n, n % 4 != 0 takes the reduction's element path); an e4m3 input with no workspace

@@ -689,3 +689,48 @@ def test_prefill_edge_cases(nhm):
     st = _check_states(spg, spr, sp, set(int(s) for s in sl))
     _check_windows(cpg, cpr, cp, set(int(s) for s in sl))
     print(f"prefill edge cases: {m}, state rel l2 {st:.3e}")
+
+
+def test_block_per_tensor_weight_scales(nhm, block0):
+    """A block whose projections carry one weight scale each (the checkpoint's form, the
+    per-tensor flag of nhm_fp8_weight) equals, bit for bit, the same block with those scales
+    broadcast to per-channel vectors: decode (B = 8, the GEMV path) and prefill (the GEMM path),
+    outputs, state pools and conv windows."""
+    from tests.gpu_util import dev, host, zeros_ws
+    from workloads import conv_pool, hidden, ssm_pool
+    p = dict(block0)
+    for key in ("in_w_scale", "out_w_scale"):
+        p[key] = np.full_like(p[key], p[key][0])               # one scale per projection
+    vec = nhm.MixerParams(nhm.Fp8Weight(dev(p["in_w"]), dev(p["in_w_scale"]), dev(p["in_a_scale"])),
+                          nhm.Fp8Weight(dev(p["out_w"]), dev(p["out_w_scale"]), dev(p["out_a_scale"])),
+                          dev(p["conv_w"]), dev(p["conv_b"]), dev(p["norm_w"]), dev(p["A_log"]), dev(p["D"]),
+                          dev(p["dt_bias"]))
+    one = nhm.MixerParams(nhm.Fp8Weight(dev(p["in_w"]), dev(p["in_w_scale"][:1].copy()), dev(p["in_a_scale"])),
+                          nhm.Fp8Weight(dev(p["out_w"]), dev(p["out_w_scale"][:1].copy()), dev(p["out_a_scale"])),
+                          dev(p["conv_w"]), dev(p["conv_b"]), dev(p["norm_w"]), dev(p["A_log"]), dev(p["D"]),
+                          dev(p["dt_bias"]))
+    sp, cp = ssm_pool(0, 3, 10), conv_pool(0, 3, 10)          # 10 slots: every index below is in range
+    h = hidden(0, 8, extra=21)
+    sl = np.array([9, 0, 4, 7, 2, 5, 1, 8], np.int32)
+    res = []
+    for prm in (vec, one):
+        lay = nhm.decode_ws_layout(8)
+        spd, cpd = dev(sp), dev(cp)
+        out = torch.empty((8, H), dtype=torch.int16, device="cuda")
+        nhm.mixer_decode(prm, dev(h), dev(sl), spd, cpd, out, zeros_ws(lay["total"]))
+        torch.cuda.synchronize()
+        res.append((host(out), host(spd), host(cpd)))
+    for x, y in zip(*res):
+        assert np.array_equal(x, y)
+    hp = hidden(0, 300, extra=22)
+    res = []
+    for prm in (vec, one):
+        lay = nhm.prefill_ws_layout(300, 2)
+        spd, cpd = dev(sp), dev(cp)
+        out = torch.empty((300, H), dtype=torch.int16, device="cuda")
+        nhm.mixer_prefill(prm, dev(hp), dev(np.array([0, 170, 300], np.int32)), dev(np.array([3, 6], np.int32)),
+                          dev(np.array([1, 0], np.int32)), spd, cpd, out, zeros_ws(lay["total"]))
+        torch.cuda.synchronize()
+        res.append((host(out), host(spd), host(cpd)))
+    for x, y in zip(*res):
+        assert np.array_equal(x, y)
