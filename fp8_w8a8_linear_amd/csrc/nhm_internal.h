@@ -23,13 +23,16 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 enum class Kern : int {
     kQuantVec8, kQuantScalar, kDequantChannel, kGemv, kRing192x128, kRing192x128Exact, kRing256x128,
     kRing256x128Exact, kRing256x256, kRing256x256Exact, kPanel64x128, kPanel64x128Exact, kTile128,
-    kTile128Exact, kSplitkReduce, kDecodeSsm, kGnormQuant, kConvFwd, kSsdState, kSsdPass, kSsdOut, kCount
+    kTile128Exact, kSplitkReduce, kDecodeSsm, kGnormQuant, kClear, kConvFwd, kSsdState, kSsdPass, kSsdOut, kCount
 };
 void count_launch(Kern k, int64_t rows);
 
 // ---- activation quant (quant.hip)
 void launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                      uint8_t* q, int64_t ld_q, hipStream_t st);
+
+// n 32-bit words set to zero (quant.hip)
+void launch_clear(uint32_t* p, int n, hipStream_t st);
 
 // per-channel e4m3 -> bf16 weight dequant (quant.hip); cols a multiple of 16, 16-byte rows
 void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_t ld_w, const float* w_scale,

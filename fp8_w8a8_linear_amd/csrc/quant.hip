@@ -120,4 +120,16 @@ void launch_dequant_channel(const uint8_t* w, int64_t rows, int64_t cols, int64_
     count_launch(Kern::kDequantChannel, rows);
 }
 
+// n 32-bit words set to zero (in place of a memset node, which a captured graph should not hold)
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+void launch_clear(uint32_t* p, int n, hipStream_t st) {
+    if (n <= 0) return;
+    const int blocks = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    clear_words_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(p, n);
+    count_launch(Kern::kClear, n);
+}
+
 }  // namespace nhm

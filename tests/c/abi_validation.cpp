@@ -34,6 +34,7 @@ nhm_status launch_gemm(const uint8_t*, int64_t, int64_t, const uint8_t*, const f
     reached("launch_gemm");
 }
 nhm_status launch_decode_ssm(const DecodeSsmArgs&, int, hipStream_t) { reached("launch_decode_ssm"); }
+void launch_clear(uint32_t*, int, hipStream_t) { reached("launch_clear"); }
 nhm_status launch_gnorm_quant(const GnormArgs&, hipStream_t) { reached("launch_gnorm_quant"); }
 nhm_status launch_prefill_mid(const PrefillArgs&, hipStream_t) { reached("launch_prefill_mid"); }
 }  // namespace nhm

@@ -127,8 +127,9 @@ def test_decode_one_block_one_token(nhm, block0):
     print(f"decode m=1: {m}, state rel l2 {st:.3e}")
 
 
-# 20: in_proj and out_proj one GEMV per 16 rows; 33 and 64: out_proj as one GEMM call with
-# split k (33: ragged m), in_proj still per 16 rows; 64 is the whole 64-slot pool in one call
+# 20: in_proj and out_proj one GEMV per 16 rows; 33 and 64: both projections as one GEMM call
+# each (in_proj summing exactly, out_proj with split k; 33: ragged m), the norm's hand-off
+# counters zeroed by a launch of their own; 64 is the whole 64-slot pool in one call
 @pytest.mark.parametrize("B,slot_list,S", [(8, None, 24), (3, [5, -1, 0], 24), (20, None, 24),
                                            (33, None, 48), (64, None, 64)])
 def test_decode_batch(nhm, block0, B, slot_list, S):
@@ -139,11 +140,18 @@ def test_decode_batch(nhm, block0, B, slot_list, S):
     sl = np.array(slot_list, np.int32) if slot_list else slots(2, B, S)
     sp, cp = ssm_pool(2, 0, S), conv_pool(2, 0, S)
     pd = upload_params(block0)
+    nhm.dispatch_counters(reset=True)
     out, spg, cpg, ws, lay = _gpu_decode(nhm, pd, h, sl, sp, cp)
+    path = nhm.dispatch_counters(reset=True)
+    if B > 32:
+        assert "gemv" not in path and path["clear"] == (1, B * 8) and path["decode_ssm"] == (1, B), path
+        assert any(k.endswith("_exact") and v == (1, B) for k, v in path.items()), path
+    else:
+        assert path["gemv"][0] == 2 * ((B + 15) // 16) and "clear" not in path, path
     spr, cpr = sp.copy(), cp.copy()
     ref, res = mixer_decode(block0, h, sl, spr, cpr)
-    # a1: the in_proj input codes kept in the workspace (quantized inside the GEMV launches of
-    # up to 16 rows each), every row, padded ones too
+    # a1: the in_proj input codes kept in the workspace (the quant launch), every row, padded
+    # ones too
     q_in = ws_region(ws, lay["q_in"], B * H, np.uint8).reshape(B, H)
     assert np.array_equal(q_in, res["q_in"].reshape(B, H))
     live = [b for b in range(B) if sl[b] >= 0]
