@@ -78,11 +78,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     // weight stream), then the weight stream, k-step by k-step.
     const float sa = *g.a_scale;
     const float sq = g.out_q ? *g.q_scale : 1.0f;
+    // per channel with n a multiple of 4: one 16-byte load per tile (this lane's four consecutive
+    // features; past n, zeros); otherwise one load per feature (index clamped; one for a
+    // per-tensor scale)
     float sc[kTiles][4];
+    if (g.ws_step != 0 && (g.n & 3) == 0) {
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w_scale, (short)0, (int)(g.n * 4), 0x00020000);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t)
+        for (int t = 0; t < kTiles; ++t) {
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(nbase[t] * 4), 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[(nbase[t] + r < g.n ? nbase[t] + r : g.n - 1) * g.ws_step];
+            for (int r = 0; r < 4; ++r) sc[t][r] = sa * __uint_as_float(v[r]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[(nbase[t] + r < g.n ? nbase[t] + r : g.n - 1) * g.ws_step];
+    }
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
