@@ -195,10 +195,13 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_state_kernel(const PrefillArg
 // loaded into registers at the start, then takes B's place in LDS for C.H_in^T, so a
 // workgroup holds 53 KB and three share a CU. The C rows of a wave's t-tile are read
 // from L2 into registers and serve as the B operand of C.B^T and the A operand of
-// C.H_in^T. G never leaves registers: C.B^T
-// is computed transposed (B as the A operand), so a lane holds G for one row t and
-// four consecutive s of each 16-wide s-tile -- an A operand of G.x once x is read
-// for the same eight s.
+// C.H_in^T. G never leaves registers: C.B^T is computed transposed (B as the A operand).
+// B's rows are staged in a permuted order -- token 32 k + 8 q + 4 h + r of a 32-token block
+// at row 32 k + 16 h + 4 q + r -- so that the accumulator lane (r16, q) of the two 16-row
+// tiles h = 0, 1 of block k holds G for row t and the eight consecutive tokens
+// 32 k + 8 q .. + 7: an A operand of G.x whose B operand, x^T for the same eight tokens, is
+// one 16-byte LDS read. The result leaves through LDS (f32 rows, B's bytes once more), so each
+// thread adds D x for eight channels of one token and stores them as one 16-byte piece.
 __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs a) {   // 6 waves per SIMD: 3 workgroups per CU
     const int t = threadIdx.x;
     int c, h;
@@ -268,8 +271,9 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
     }
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
-        const int e = t + i * kThreads, s = e >> 4, n8 = e & 15;
-        *reinterpret_cast<uint4*>(&s_b[s * kLd + n8 * 8]) = s < L ? bv[i] : make_uint4(0u, 0u, 0u, 0u);
+        const int e = t + i * kThreads, s = e >> 4, n8 = e & 15, u = s & 31;
+        const int row = (s & ~31) + 16 * ((u >> 2) & 1) + 4 * (u >> 3) + (u & 3);
+        *reinterpret_cast<uint4*>(&s_b[row * kLd + n8 * 8]) = s < L ? bv[i] : make_uint4(0u, 0u, 0u, 0u);
     }
     if (!tok) {
 #pragma unroll
@@ -284,23 +288,22 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
     for (int pj = 0; pj < 4; ++pj) acc1[pj] = acc2[pj] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (live) {
-        // y1 = G x over the 32-wide s blocks kk with 32 kk <= 16 ti + 15
+        // y1 = G x over the 32-token blocks kk with 32 kk <= 16 ti + 15 (both 16-row tiles of
+        // a block hold tokens up to its end, so neither is skipped)
         const int nkk = (16 * ti + 15) / 32 + 1;
         for (int kk = 0; kk < nkk; ++kk) {
             float gv[8];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int sj = 2 * kk + half;               // s-tile
+                const int sj = 2 * kk + half;               // LDS row tile
                 v4f cb = {0.f, 0.f, 0.f, 0.f};
-                if (sj <= ti) {
 #pragma unroll
-                    for (int kn = 0; kn < kDS / 32; ++kn)
-                        cb = mfma_bf16(lds8(&s_b[(16 * sj + r16) * kLd + kn * 32 + q * 8]), cop[kn], cb);
-                }
-                // cb[r] = (C.B^T)[t = trow][s = 16 sj + 4 q + r]
+                for (int kn = 0; kn < kDS / 32; ++kn)
+                    cb = mfma_bf16(lds8(&s_b[(16 * sj + r16) * kLd + kn * 32 + q * 8]), cop[kn], cb);
+                // cb[r] = (C.B^T)[t = trow][token sc]
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int sc = 16 * sj + 4 * q + r;
+                    const int sc = 32 * kk + 8 * q + 4 * half + r;
                     gv[4 * half + r] = (sc <= trow && tok) ? cb[r] * __expf(cs_t - s_cs[sc]) * s_dt[sc] : 0.f;
                 }
             }
@@ -312,13 +315,10 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
                 gh[j] = hi;
                 gl[j] = lo;
             }
-            // B operand: x[s][p] for the same eight s, p = 16 pj + r16
+            // B operand: x[s][p] for the same eight tokens, p = 16 pj + r16
 #pragma unroll
             for (int pj = 0; pj < 4; ++pj) {
-                const uint16_t* xr = &s_xt[(16 * pj + r16) * kLd + 32 * kk + 4 * q];
-                const uint2 lo = *reinterpret_cast<const uint2*>(xr);
-                const uint2 hi = *reinterpret_cast<const uint2*>(xr + 16);
-                const bf16x8 xb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                const bf16x8 xb = lds8(&s_xt[(16 * pj + r16) * kLd + 32 * kk + 8 * q]);
                 acc1[pj] = mfma_bf16(gh, xb, acc1[pj]);
                 acc1[pj] = mfma_bf16(gl, xb, acc1[pj]);
             }
@@ -340,30 +340,57 @@ __global__ __launch_bounds__(kThreads, 6) void ssd_out_kernel(const PrefillArgs 
             make_uint2(bits(lo[0]) | ((uint32_t)bits(lo[1]) << 16), bits(lo[2]) | ((uint32_t)bits(lo[3]) << 16));
     }
     __syncthreads();
-    if (!live) return;
-    // y2 = C H_in^T
+    // this thread's x for D x: token rows t / 8 and 64 + t / 8, channels 8 (t % 8) .. + 7 of the
+    // head (rows past L read row L - 1 and are not stored)
+    const int yc = 8 * (t & 7);
+    uint4 xd[2];
 #pragma unroll
-    for (int pj = 0; pj < 4; ++pj) {
-#pragma unroll
-        for (int kn = 0; kn < kDS / 32; ++kn) {
-            const int off = (16 * pj + r16) * kLd + kn * 32 + q * 8;
-            acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hh[off]), acc2[pj]);
-            acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hl[off]), acc2[pj]);
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int row = (t >> 3) + 64 * i;
+        xd[i] = *reinterpret_cast<const uint4*>(a.xbc_conv + (tok0 + (row < L ? row : L - 1)) * a.conv_dim + h * kHP + yc);
     }
-    // acc[r] = Y[t = 16 ti + 4 q + r][p = 16 pj + r16]
-    const float Dh = a.D[h];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * ti + 4 * q + r;
-        if (tr >= L) continue;
-        const float e = __expf(s_cs[tr]);
+    if (live) {   // y2 = C H_in^T
 #pragma unroll
         for (int pj = 0; pj < 4; ++pj) {
-            const int pc = 16 * pj + r16;
-            const float xv = bf16_to_f32(s_xt[pc * kLd + tr]);
-            a.y[(tok0 + tr) * a.d_inner + h * kHP + pc] = (uint16_t)f32_to_bf16(acc1[pj][r] + e * acc2[pj][r] + Dh * xv);
+#pragma unroll
+            for (int kn = 0; kn < kDS / 32; ++kn) {
+                const int off = (16 * pj + r16) * kLd + kn * 32 + q * 8;
+                acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hh[off]), acc2[pj]);
+                acc2[pj] = mfma_bf16(cop[kn], lds8(&s_hl[off]), acc2[pj]);
+            }
         }
+    }
+    __syncthreads();   // every wave is done with H_in
+    // acc[r] = Y[t = 16 ti + 4 q + r][p = 16 pj + r16]: G x + exp(cs_t) C H_in^T as f32 rows of
+    // kYs floats in B's bytes
+    constexpr int kYs = kHP + 4;
+    static_assert(kQ * kYs * 4 <= kQ * kLd * 2, "the f32 result rows fit where B was");
+    float* const s_y = reinterpret_cast<float*>(s_b);
+    if (live) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tr = 16 * ti + 4 * q + r;
+            const float e = __expf(s_cs[tr]);
+#pragma unroll
+            for (int pj = 0; pj < 4; ++pj) s_y[tr * kYs + 16 * pj + r16] = acc1[pj][r] + e * acc2[pj][r];
+        }
+    }
+    __syncthreads();
+    const float Dh = a.D[h];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (t >> 3) + 64 * i;
+        if (row >= L) continue;
+        const float4 y0 = *reinterpret_cast<const float4*>(&s_y[row * kYs + yc]);
+        const float4 y1 = *reinterpret_cast<const float4*>(&s_y[row * kYs + yc + 4]);
+        float xf[8];
+        unpack8(xd[i], xf);
+        const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = f32_to_bf16(yv[2 * j] + Dh * xf[2 * j]) | (f32_to_bf16(yv[2 * j + 1] + Dh * xf[2 * j + 1]) << 16);
+        *reinterpret_cast<uint4*>(a.y + (tok0 + row) * a.d_inner + h * kHP + yc) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
