@@ -125,6 +125,15 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a, int 
     }
     int i = seq_of(a.cu_seqlens, a.n_seqs, t0);
     int64_t s0 = a.cu_seqlens[i];
+    // The run's rows are loaded before any is used (rows past T read row T - 1, unused): the
+    // compiler cannot move a load above an earlier iteration's store, so loads inside the loop
+    // would wait one memory latency per token.
+    uint4 xr[kConvRun];
+#pragma unroll
+    for (int r = 0; r < kConvRun; ++r) {
+        const int64_t tok = t0 + r < a.T ? t0 + r : a.T - 1;
+        xr[r] = *reinterpret_cast<const uint4*>(src + tok * a.d_in_proj);
+    }
     float u[3][8];
 #pragma unroll
     for (int j = 1; j <= 3; ++j) {
@@ -133,16 +142,21 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const PrefillArgs a, int 
                             : init_row(a, i, (int)(3 + tok - s0), c8);
         unpack8(v, u[3 - j]);
     }
+    // the start of the next sequence, held in a register (a load in the loop would wait behind
+    // the previous token's store)
+    int64_t next = i < a.n_seqs - 1 ? a.cu_seqlens[i + 1] : INT64_MAX;
+#pragma unroll
     for (int r = 0; r < kConvRun; ++r) {
         const int64_t tok = t0 + r;
         if (tok >= a.T) break;
-        if (i < a.n_seqs - 1 && tok >= a.cu_seqlens[i + 1]) {   // the next non-empty sequence starts here
+        if (tok >= next) {   // the next non-empty sequence starts here
             while (i < a.n_seqs - 1 && tok >= a.cu_seqlens[i + 1]) ++i;
+            next = i < a.n_seqs - 1 ? a.cu_seqlens[i + 1] : INT64_MAX;
 #pragma unroll
             for (int j = 0; j < 3; ++j) unpack8(init_row(a, i, j, c8), u[j]);
         }
         float x[8];
-        unpack8(*reinterpret_cast<const uint4*>(src + tok * a.d_in_proj), x);
+        unpack8(xr[r], x);
         uint32_t ob[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
