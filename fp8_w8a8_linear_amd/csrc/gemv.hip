@@ -53,7 +53,7 @@ constexpr int kStreamAux = 0;
 
 template <int kWaves, int kSteps, int kTiles, bool kLines>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
-    __shared__ v4f s_red[kWaves - 1][kTiles][64];
+    __shared__ v4f s_red[kWaves][kTiles][64];   // every wave's partial of every row tile
     // kLines: this wave's transpose buffer, one k-step of the 16 kTiles rows
     __shared__ __attribute__((aligned(16))) uint8_t s_tr[kLines ? kWaves : 1][kLines ? 16 * kTiles * 128 : 16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -66,10 +66,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     const int col = lane & 15;                  // B operand column (token)
     const int kq = (lane >> 4) * 32;
     // MFMA row tile t covers features n0 + 16 t .. + 15 (A operand row lane % 16; rows at or
-    // past nend load zeros); its result lane holds features nbase[t] .. + 3 of token col
-    int64_t nbase[kTiles];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) nbase[t] = n0 + 16 * t + 4 * (lane >> 4);
+    // past nend load zeros); its result lane holds features n0 + 16 t + 4 (lane / 16) .. + 3 of
+    // token col. Wave t < kTiles finishes row tile t: its result lane's features start at nb.
+    const int64_t nb = n0 + 16 * (wave < kTiles ? wave : 0) + 4 * (lane >> 4);
 
     // Everything up to the MFMAs is straight-line code: loads past the operands go to an
     // out-of-range buffer offset (zeros) and indexes are clamped, so the compiler can wait
@@ -78,23 +77,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     // weight stream), then the weight stream, k-step by k-step.
     const float sa = *g.a_scale;
     const float sq = g.out_q ? *g.q_scale : 1.0f;
-    // per channel with n a multiple of 4: one 16-byte load per tile (this lane's four consecutive
-    // features; past n, zeros); otherwise one load per feature (index clamped; one for a
-    // per-tensor scale)
-    float sc[kTiles][4];
+    // the scales of this wave's row tile: per channel with n a multiple of 4, one 16-byte load
+    // (this lane's four consecutive features; past n, zeros); otherwise one load per feature
+    // (index clamped; one for a per-tensor scale)
+    float sc[4];
     if (g.ws_step != 0 && (g.n & 3) == 0) {
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w_scale, (short)0, (int)(g.n * 4), 0x00020000);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(nb * 4), 0, 0);
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(nbase[t] * 4), 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[t][r] = sa * __uint_as_float(v[r]);
-        }
+        for (int r = 0; r < 4; ++r) sc[r] = sa * __uint_as_float(v[r]);
     } else {
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[t][r] = sa * g.w_scale[(nbase[t] + r < g.n ? nbase[t] + r : g.n - 1) * g.ws_step];
+        for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[(nb + r < g.n ? nb + r : g.n - 1) * g.ws_step];
     }
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
@@ -177,37 +171,32 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
         }
     }
 
-    if (wave > 0) {
+    // The partial tiles go through LDS; wave t sums row tile t over the waves in wave order
+    // (deterministic) and stores it, so the row tiles' epilogues run side by side.
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) s_red[wave - 1][t][lane] = acc[t];
-    }
+    for (int t = 0; t < kTiles; ++t) s_red[wave][t][lane] = acc[t];
     __syncthreads();
-    if (wave > 0) return;
+    if (wave >= kTiles) return;
+    v4f d = s_red[0][wave][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) acc[t] += s_red[w - 1][t][lane];
+    for (int w = 1; w < kWaves; ++w) d += s_red[w][wave][lane];
 
-    // acc[t][r] = D[feature nbase[t] + r][token col]
-    if (col >= g.m) return;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-        const int64_t nb = nbase[t];
-        if (nb >= nend) break;   // row tiles are in feature order
+    // d[r] = D[feature nb + r][token col]
+    if (col >= g.m || nb >= nend) return;
+    {
         if (g.out_f32) {
             float* of = g.out_f32 + (int64_t)col * g.ld_out + nb;
             if (g.vec_out && (nb & 3) == 0 && nb + 3 < nend) {
-                *reinterpret_cast<float4*>(of) =
-                    make_float4(acc[t][0] * sc[t][0], acc[t][1] * sc[t][1], acc[t][2] * sc[t][2], acc[t][3] * sc[t][3]);
+                *reinterpret_cast<float4*>(of) = make_float4(d[0] * sc[0], d[1] * sc[1], d[2] * sc[2], d[3] * sc[3]);
             } else {
                 for (int r = 0; r < 4; ++r)
-                    if (nb + r < nend) of[r] = acc[t][r] * sc[t][r];
+                    if (nb + r < nend) of[r] = d[r] * sc[r];
             }
-            continue;
+            return;
         }
         uint32_t hb[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(acc[t][r] * sc[t][r]);
+        for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16(d[r] * sc[r]);
         uint16_t* o = g.out + (int64_t)col * g.ld_out + nb;
         if (g.vec_out && (nb & 3) == 0 && nb + 3 < nend) {
             *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
