@@ -630,6 +630,87 @@ def test_prefill_small_geometry(nhm):
     print(f"prefill small geometry {lens}: {m}")
 
 
+# A third geometry: hidden 256, 16 heads of 64 in one group, so every head shares one B/C
+# group and a norm group spans 1,024 channels. The decode state kernel finishes norm groups of
+# at most 512 channels itself; wider ones go to a launch of their own (with the B/C window
+# shift), which these tests reach.
+WIDE = dict(hidden=256, n_heads=16, head_dim=64, d_state=128, n_groups=1, conv_width=4, rms_eps=1e-5)
+
+
+def _geom_parity(g, out, ws, lay, rows, T, ref, ref_norm, ref_q, p):
+    from tests.gpu_util import block_parity, ws_region
+    inner = g["n_heads"] * g["head_dim"]
+    q = ws_region(ws, lay["q_out"], T * inner, np.uint8).reshape(T, inner)[rows]
+    nrm = ws_region(ws, lay["norm"], T * inner, np.uint16).reshape(T, inner)[rows]
+    return block_parity(out[rows], q, nrm, ref[rows], ref_norm, ref_q, p)
+
+
+def test_decode_wide_group(nhm):
+    """Decode with one 1,024-channel norm group (16 heads, hidden 256), with a padded row: the
+    norm runs as its own launch."""
+    from oracle import mixer_decode
+    from tests.gpu_util import dev, host, upload_params, ws_region, zeros_ws
+    from workloads import block_params, conv_pool, hidden, ssm_pool
+    g, S, B = WIDE, 9, 5
+    p = block_params(7, 0, g)
+    h = hidden(7, B, g)
+    sl = np.array([6, -1, 2, 8, 0], np.int32)
+    sp, cp = ssm_pool(7, 0, S, g=g), conv_pool(7, 0, S, g=g)
+    pd = upload_params(p, g)
+    lay = nhm.decode_ws_layout(B, g)
+    ws = zeros_ws(lay["total"])
+    spd, cpd = dev(sp), dev(cp)
+    out = torch.empty((B, g["hidden"]), dtype=torch.int16, device="cuda")
+    nhm.dispatch_counters(reset=True)
+    nhm.mixer_decode(pd, dev(h), dev(sl), spd, cpd, out, ws)
+    torch.cuda.synchronize()
+    path = nhm.dispatch_counters(reset=True)
+    assert "gnorm_quant" in path and "decode_ssm" in path, path
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_decode(p, h, sl, spr, cpr, g=g)
+    q_in = ws_region(ws, lay["q_in"], B * g["hidden"], np.uint8).reshape(B, g["hidden"])
+    assert np.array_equal(q_in, res["q_in"].reshape(B, g["hidden"]))
+    o = host(out)
+    live = [b for b in range(B) if sl[b] >= 0]
+    m = _geom_parity(g, o, ws, lay, live, B, ref, res["norm"][live], res["q_out"][live], p)
+    assert np.all(o[1] == 0)
+    touched = {int(s) for s in sl if s >= 0}
+    _check_states(host(spd), spr, sp, touched)
+    _check_windows(host(cpd), cpr, cp, touched)
+    print(f"decode wide group: {m}, path {path}")
+
+
+def test_prefill_wide_group(nhm):
+    """Varlen prefill with one 1,024-channel norm group: a two-chunk sequence from a carried
+    state, a fresh one and a one-token continuation."""
+    from oracle import mixer_prefill
+    from tests.gpu_util import dev, host, upload_params, zeros_ws
+    from workloads import block_params, conv_pool, hidden, ssm_pool
+    g, S = WIDE, 7
+    lens, has_init = [131, 3, 1], [1, 0, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    p = block_params(8, 0, g)
+    h = hidden(8, T, g)
+    sl = np.array([5, 1, 3], np.int32)
+    sp, cp = ssm_pool(8, 0, S, g=g), conv_pool(8, 0, S, g=g)
+    pd = upload_params(p, g)
+    lay = nhm.prefill_ws_layout(T, len(lens), g=g)
+    ws = zeros_ws(lay["total"])
+    spd, cpd = dev(sp), dev(cp)
+    out = torch.empty((T, g["hidden"]), dtype=torch.int16, device="cuda")
+    nhm.mixer_prefill(pd, dev(h), dev(cu), dev(sl), dev(np.asarray(has_init, np.int32)), spd, cpd, out, ws)
+    torch.cuda.synchronize()
+    spr, cpr = sp.copy(), cp.copy()
+    ref, res = mixer_prefill(p, h, cu, sl, has_init, spr, cpr, g=g)
+    norm, q, _ = _prefill_refs(res, lens)
+    m = _geom_parity(g, host(out), ws, lay, list(range(T)), T, ref, norm, q, p)
+    touched = {int(s) for s in sl}
+    _check_states(host(spd), spr, sp, touched)
+    _check_windows(host(cpd), cpr, cp, touched)
+    print(f"prefill wide group {lens}: {m}")
+
+
 def _edge_params():
     """Block 0's parameters with the method's corner cases switched on: heads 0-7 have
     dt_raw + dt_bias > 20 (softplus taken as its argument), head 8 A_log = 0 (A = -1) and head 9
