@@ -377,6 +377,16 @@ def main():
     rhi = up(np.zeros(len(rl), np.int32))
     rws = torch.zeros(nhm.prefill_ws_layout(RT, len(rl))["total"], dtype=torch.uint8, device=dev)
     rout = torch.empty((RT, HIDDEN), dtype=torch.int16, device=dev)
+    # the kernels one eager call launches (has_initial = 0: the call reads none of the pools
+    # it writes, so the replays below compute the same block)
+    nhm.dispatch_counters(reset=True)
+    nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws)
+    torch.cuda.synchronize()
+    ragged_path = nhm.dispatch_counters(reset=True)
+    for k_ in ("quant_vec8", "gemm_ring256x256_exact", "gemm_ring256x256", "conv_fwd", "ssd_state", "ssd_pass",
+               "ssd_out", "gnorm_quant"):
+        assert k_ in ragged_path, f"the ragged prefill did not launch {k_}: {ragged_path}"
+    log(f"ragged prefill path: {ragged_path}")
     rgr = graph_of(lambda: nhm.mixer_prefill(rpar, rh, rcu, rsl, rhi, rsp, rcp, rout, rws))
     for _ in range(2):
         rgr.replay()
@@ -465,7 +475,7 @@ def main():
         "gemm_m15360": gemm_large,
         "linear_sweep": sweep,
         "prefill_ragged_15360": {"lengths": rl, "us_per_block": round(rag_us, 1), "repeats_us": rag_all,
-                                 "tokens_per_s": round(RT / (rag_us * 1e-6), 1)},
+                                 "tokens_per_s": round(RT / (rag_us * 1e-6), 1), "path": ragged_path},
         "parity_sample": parity,
         "cpu_baseline": cpu,
     }
