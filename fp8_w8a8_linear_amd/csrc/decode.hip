@@ -53,30 +53,6 @@ __device__ __forceinline__ void store_state(v4f* st, v2u* st16, int i, const v4f
         __builtin_nontemporal_store(v, st + i);
 }
 
-// Lane sums by DPP (VALU lane moves) instead of LDS-crossbar permutes, which take an LDS round
-// trip per step. half_sum: four in-row steps (quad xor 1 and xor 2, then each row's halves
-// and quarters mirrored onto each other) leave every lane with its row's sum; row 1 (3) then
-// adds lane 15 of row 0 (2), so lanes 31 and 63 hold the sums of their 32-lane halves (other
-// lanes hold partial sums). wave_total: row_bcast:31 then adds lane 31 into rows 2 and 3, and
-// lane 63's total goes to every lane.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_add(float v) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, false));
-}
-
-__device__ __forceinline__ float half_sum(float v) {
-    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
-    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
-    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
-    v = dpp_add<0x140, 0xF>(v);   // row_mirror
-    return dpp_add<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
-}
-
-__device__ __forceinline__ float wave_total(float v) {
-    v = dpp_add<0x143, 0xC>(half_sum(v));   // row_bcast:31 into rows 2 and 3
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // The cache policy of the y hand-off: stores written through to, and loads served from, the
 // device-coherent level (sc0 sc1).
 constexpr int kCoherent = 0x11;
@@ -238,7 +214,7 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
             v1 = bf16_to_f32(yy >> 16) * silu(bf16_to_f32(zz >> 16));
             ss = v0 * v0 + v1 * v1;
         }
-        ss = wave_total(ss);
+        ss = wave_sum(ss);
         if ((t & 63) == 0) s_ss[t >> 6] = ss;
         __syncthreads();
         ss = s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3];

@@ -125,10 +125,47 @@ __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcp
 __device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(__expf(u)); }
 
 // Sum over the 64 lanes of a wave; every lane receives the total.
+// Lane sums by DPP (VALU lane moves within rows of 16 lanes, and row_bcast across rows)
+// instead of LDS-crossbar permutes, which take an LDS round trip per step.
+// dpp_take: lane i's view of another lane's v under the DPP control; 0 where the row or bank
+// mask leaves lane i out or the source lies outside its row.
+template <int kCtrl, int kRowMask = 0xF, int kBankMask = 0xF>
+__device__ __forceinline__ float dpp_take(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, kBankMask, false));
+}
+
+// Sums over each 32-lane half: four in-row steps (quad xor 1 and xor 2, then each row's halves
+// and quarters mirrored onto each other) leave every lane with its row's sum; row 1 (3) then adds
+// lane 15 of row 0 (2). Lanes 31 and 63 hold their halves' sums (other lanes partial sums).
+__device__ __forceinline__ float half_sum(float v) {
+    v += dpp_take<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+    v += dpp_take<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+    v += dpp_take<0x141>(v);     // row_half_mirror
+    v += dpp_take<0x140>(v);     // row_mirror
+    return v + dpp_take<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+}
+
+// The sum over the wave, in every lane: row_bcast:31 adds lane 31 into rows 2 and 3, and lane
+// 63's total is read out.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v = half_sum(v);
+    v += dpp_take<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Inclusive prefix sum over the wave's 64 lanes: within each row the sums of the last 4 lanes
+// (shifts by 1, 2, 3 of the original values), then shifts by 4 (lanes 4-15) and 8 (lanes 8-15)
+// of those partial sums; then row_bcast carries row 0's (2's) total into row 1 (3), and lane
+// 31's into rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    const float v0 = v;
+    v += dpp_take<0x111>(v0);              // row_shr:1
+    v += dpp_take<0x112>(v0);              // row_shr:2
+    v += dpp_take<0x113>(v0);              // row_shr:3
+    v += dpp_take<0x114, 0xF, 0xE>(v);     // row_shr:4, lanes 4-15 of each row
+    v += dpp_take<0x118, 0xF, 0xC>(v);     // row_shr:8, lanes 8-15 of each row
+    v += dpp_take<0x142, 0xA>(v);          // row_bcast:15 into rows 1 and 3
+    return v + dpp_take<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
 }
 
 // 16x16x128 e4m3 MFMA, f32 accumulate (gfx950). Lane l supplies row (l % 16) of A

@@ -42,22 +42,17 @@ __device__ __forceinline__ uint16_t bits(__bf16 v) { return __builtin_bit_cast(u
 // dt_s = softplus(dt_raw + bias) (zero beyond L) and the inclusive scan cs_s of dt_s * A
 // over the chunk, in s_dt / s_cs, for the raw value u that thread s < Q loaded; also
 // stored for the other kernels. Threads 0..127 are waves 0 and 1: each scans its 64
-// values with lane shuffles, then wave 1 adds wave 0's total. Ends with a barrier.
+// values with DPP lane moves, then wave 1 adds wave 0's total. Ends with a barrier.
 // u: the token's raw dt (bf16 widened); dt_bias, a_log: the head's parameters, loaded by the
 // caller ahead of its bulk loads.
 __device__ __forceinline__ void chunk_decay(const PrefillArgs& a, int c, int h, int L, float u, float dt_bias,
                                             float a_log, float* s_dt, float* s_cs) {
-    const int t = threadIdx.x, lane = t & 63;
+    const int t = threadIdx.x;
     __shared__ float s_w0;
     float dt = 0.f, v = 0.f;
     if (t < kQ) {
         dt = t < L ? softplus(u + dt_bias) : 0.f;
-        v = dt * -__expf(a_log);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float w = __shfl_up(v, o, 64);
-            if (lane >= o) v += w;
-        }
+        v = wave_prefix_sum(dt * -__expf(a_log));
         if (t == 63) s_w0 = v;
     }
     __syncthreads();
