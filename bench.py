@@ -60,7 +60,7 @@ def decode_bytes_per_layer(B, state_bytes=4):
 # the same counter reads for the 256 MiB device copy of that run. Valid only for the kernel
 # sources it was measured on: reported as null once their hash differs.
 TRAFFIC = {"sources": ["fp8_w8a8_linear_amd/csrc/gemv.hip", "fp8_w8a8_linear_amd/csrc/nhm_device.h"],
-           "sha256": "b0ba6b9b44b48415f6f0ea643a6377ff5428da8efe6c44c888e3656e5224a63f",
+           "sha256": "7a4c2d3d7e006fbf10927e27c3569a69167c2c542c38a2a465b0ab4f33e65223",
            "bytes_per_launch": 28210252}
 
 
