@@ -35,9 +35,15 @@ def flags():
             "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source flags. decode.hip: the compiler's atomic optimizer wraps the norm hand-off's
+# counter increment in a wave-level aggregate whose result it reads right away, so the wave
+# waited for the atomic's round trip before issuing the state stores meant to overlap it.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
