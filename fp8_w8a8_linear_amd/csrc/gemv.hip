@@ -77,19 +77,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
     // weight stream), then the weight stream, k-step by k-step.
     const float sa = *g.a_scale;
     const float sq = g.out_q ? *g.q_scale : 1.0f;
-    // the scales of this wave's row tile: per channel with n a multiple of 4, one 16-byte load
-    // (this lane's four consecutive features; past n, zeros); otherwise one load per feature
-    // (index clamped; one for a per-tensor scale)
-    float sc[4];
-    if (g.ws_step != 0 && (g.n & 3) == 0) {
-        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w_scale, (short)0, (int)(g.n * 4), 0x00020000);
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(nb * 4), 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = sa * __uint_as_float(v[r]);
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = sa * g.w_scale[(nb + r < g.n ? nb + r : g.n - 1) * g.ws_step];
-    }
+    // the weight scales of this wave's row tile, one 16-byte load with no branch around it: per
+    // channel, this lane's four consecutive features (zeros past n); per tensor, the one scale in
+    // the first word of a one-word range. They are applied in the epilogue; using them here (the
+    // product with sa under a branch) made the wave wait for this load before its weight stream.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.w_scale, (short)0, g.ws_step != 0 ? (int)(g.n * 4) : 4, 0x00020000);
+    const v4u sraw = __builtin_amdgcn_raw_buffer_load_b128(srs, g.ws_step != 0 ? (uint32_t)(nb * 4) : 0u, 0, 0);
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
@@ -183,6 +177,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs g) {
 
     // d[r] = D[feature nb + r][token col]
     if (col >= g.m || nb >= nend) return;
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = sa * __uint_as_float(g.ws_step != 0 ? sraw[r] : sraw[0]);
     {
         if (g.out_f32) {
             float* of = g.out_f32 + (int64_t)col * g.ld_out + nb;
