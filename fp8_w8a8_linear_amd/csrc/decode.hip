@@ -133,6 +133,9 @@ __global__ __launch_bounds__(256) void decode_ssm_kernel(const DecodeSsmArgs a) 
             hv[i] = __builtin_nontemporal_load(st + t + 256 * i);
         }
     }
+    // every state load is issued before the conv below, whose arithmetic waits for the small
+    // loads (scheduled among the state loads, it held the state stream back by their round trip)
+    __builtin_amdgcn_sched_barrier(0);
 
     const uint32_t xo = conv4_silu(xbias, xtap, x0, x1, x2, xcur);
     const uint32_t bo = conv4_silu(bbias, btap, b0, b1, b2, bcur);
