@@ -8,8 +8,8 @@
 //
 // Three kernels:
 //  * panel kernel (m up to 640 where the ring tiles are too few to fill the chip; 64 x 128
-//    tiles): a workgroup owns a BN-row panel of
-//    the weight and a BM-row tile of the activations. Each of its 4 waves streams
+//    tiles, or narrower weight panels where those fill the chip better): a workgroup owns a
+//    panel of up to BN weight rows and a BM-row tile of the activations. Each of its 4 waves streams
 //    its own WN weight rows straight from memory into MFMA registers, two k-steps
 //    ahead; only the activation tile, which all 4 waves share, is staged in LDS
 //    (three buffers: the operands of step k+1 are read while the MFMAs of step k
@@ -48,6 +48,7 @@ struct GemmArgs {
     int ksplit = 1;
     float* part = nullptr;
     int ws_step = 1;    // weight scale index step: 1 per channel, 0 per tensor
+    int panel_rows = 0; // panel kernel: weight rows per panel (0: all of its waves' rows)
 };
 
 // Row r of a 128-byte-wide LDS tile holds its 16-byte chunk c at slot c ^ (r & 7):
@@ -128,11 +129,15 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, q = lane >> 4, r16 = lane & 15;
     // Tile order: blocks are dealt to the 8 XCDs round robin (block b runs on XCD b % 8),
     // so consecutive blocks of one XCD walk the m-tiles of one weight panel.
-    const int npan = (int)((g.n + BN - 1) / BN), nmt = (int)((g.m + BM - 1) / BM);
+    // A panel holds PW <= BN weight rows; the waves' rows past its end load nothing (out of
+    // range) and store nothing.
+    const int PW = g.panel_rows > 0 ? g.panel_rows : BN;
+    const int npan = (int)((g.n + PW - 1) / PW), nmt = (int)((g.m + BM - 1) / BM);
     const int loc = blockIdx.x >> 3;
     const int pan = (loc / nmt) * 8 + (blockIdx.x & 7), mt = loc % nmt;
     if (pan >= npan) return;
-    const int64_t m0 = (int64_t)mt * BM, nw0 = (int64_t)pan * BN + wave * WN;
+    const int64_t pend = min((int64_t)(pan + 1) * PW, g.n);
+    const int64_t m0 = (int64_t)mt * BM, nw0 = (int64_t)pan * PW + wave * WN;
     const int nk = (int)((g.k + 127) / 128);
     const int ns = (nk + 1) & ~1;   // steps, padded to the unroll of 2 (padding steps read zeros)
 
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
         const int64_t row = nw0 + i * 16 + r16;
-        woff[i] = row < g.n ? (uint32_t)(row * g.k + 16 * q) : kOutOfRange;
+        woff[i] = row < pend ? (uint32_t)(row * g.k + 16 * q) : kOutOfRange;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t c = nw0 + i * 16 + 4 * q + r;
@@ -231,18 +236,18 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
     }
 
     const float sa = *g.a_scale;
-    const bool full = g.vec_out && m0 + BM <= g.m && nw0 + WN <= g.n;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
+        const bool full = g.vec_out && m0 + BM <= g.m && nw0 + 16 * (i + 1) <= pend;
         float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = sa * wsc[i][r];
 #pragma unroll
         for (int j = 0; j < TM; ++j)
             if (g.out_f32)
-                store_tile_f32(g.out_f32, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, g.n, acc[i][j], sc, full);
+                store_tile_f32(g.out_f32, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, pend, acc[i][j], sc, full);
             else
-                store_tile(g.out, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, g.n, acc[i][j], sc, full);
+                store_tile(g.out, g.ld_out, m0 + j * 16 + r16, nw0 + i * 16 + 4 * q, g.m, pend, acc[i][j], sc, full);
     }
 }
 
@@ -846,9 +851,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
 
 // ---------------------------------------------------------------- dispatch
 
+// Rows per weight panel: each workgroup pulls its BM activation rows and its panel's weight
+// rows over all of k, and a CU's operand delivery rate is bounded, so the busiest CU's bytes,
+// (rounds of 256 workgroups) x (BM + rows), set the time. Narrower panels (a multiple of 4
+// rows, at least 64) are taken where they leave fewer such bytes: at 512 x 2688 x 4096, 84-row
+// panels fill the chip with 256 workgroups of 148 rows instead of 168 of 192.
+static int panel_rows(int64_t m, int64_t n, int BM, int BN) {
+    const int64_t nmt = (m + BM - 1) / BM;
+    auto cost = [&](int pw) {
+        const int64_t wgs = 8 * nmt * (((n + pw - 1) / pw + 7) / 8);
+        return ((wgs + 255) / 256) * (BM + pw);
+    };
+    int best = BN;
+    for (int pw = BN - 4; pw >= 64; pw -= 4)
+        if (cost(pw) < cost(best)) best = pw;
+    return best;
+}
+
 template <int BM, int WN, bool kExact>
-static void launch_panel(const GemmArgs& g, hipStream_t st) {
-    const int64_t npan = (g.n + 4 * WN - 1) / (4 * WN), nmt = (g.m + BM - 1) / BM;
+static void launch_panel(GemmArgs g, hipStream_t st) {
+    g.panel_rows = panel_rows(g.m, g.n, BM, 4 * WN);
+    const int64_t npan = (g.n + g.panel_rows - 1) / g.panel_rows, nmt = (g.m + BM - 1) / BM;
     panel_kernel<BM, WN, kExact><<<dim3((unsigned)(8 * nmt * ((npan + 7) / 8))), dim3(256), 0, st>>>(g);
     count_launch(kExact ? Kern::kPanel64x128Exact : Kern::kPanel64x128, g.m);
 }
