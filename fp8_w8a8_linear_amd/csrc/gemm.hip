@@ -112,7 +112,6 @@ __device__ __forceinline__ v4f mfma16_step(const v8i& a, const v8i& b, const v4f
 
 // ---------------------------------------------------------------- panel kernel
 
-constexpr int kPanelDepth = 2;   // weight k-steps in flight per wave (and activation tiles in registers)
 
 __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t off) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -120,9 +119,11 @@ __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;   // past every buffer range used here (< 2^31 bytes)
 
-template <int BM, int WN, bool kExact>
+// D: weight k-steps in flight per wave (and activation tiles in registers).
+template <int BM, int WN, bool kExact, int D>
 __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
-    constexpr int BN = 4 * WN, TN = WN / 16, TM = BM / 16, D = kPanelDepth;
+    constexpr int BN = 4 * WN, TN = WN / 16, TM = BM / 16;
+    constexpr int U = D % 2 == 0 ? D : 2 * D;   // loop unroll: step kt's registers are slot kt % D
     constexpr int LA = BM * 8 / 256;   // 16-byte chunks of the activation tile per thread
     static_assert(WN % 16 == 0 && BM % 32 == 0, "tile shape");
     __shared__ __attribute__((aligned(16))) uint8_t sA[3][BM * 128];
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
     const int64_t pend = min((int64_t)(pan + 1) * PW, g.n);
     const int64_t m0 = (int64_t)mt * BM, nw0 = (int64_t)pan * PW + wave * WN;
     const int nk = (int)((g.k + 127) / 128);
-    const int ns = (nk + 1) & ~1;   // steps, padded to the unroll of 2 (padding steps read zeros)
+    const int ns = (nk + U - 1) / U * U;   // steps, padded to the unroll (padding steps read zeros)
 
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)g.w, (short)0, (int)(g.n * g.k), 0x00020000);
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.m * g.lda), 0x00020000);
@@ -215,9 +216,9 @@ __global__ __launch_bounds__(256) void panel_kernel(const GemmArgs g) {
     // Step kt: operands of kt in bop[kt & 1]; LDS buffer b1 holds tile kt+1, b2 receives kt+2
     // (its previous tile, kt-1, was read two steps ago, before the last barrier).
     int b1 = 1, b2 = 2;
-    for (int kt0 = 0; kt0 < ns; kt0 += 2) {
+    for (int kt0 = 0; kt0 < ns; kt0 += U) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int kt = kt0 + u;
             opread(b1, bop[(u + 1) & 1]);
 #pragma unroll
@@ -868,11 +869,21 @@ static int panel_rows(int64_t m, int64_t n, int BM, int BN) {
     return best;
 }
 
+// Prefetch depth: four k-steps in flight per wave on the e4m3 MFMA where k is a whole number
+// of four-step groups (at 512 x 2688 x 4096 23.6 -> 23.1 us, 128 x 2688 x 4096 19.5 -> 18.0;
+// where four-step padding was needed, as at k = 2688, it lost), else two; exact sums keep two,
+// as their conversions leave no registers for more.
 template <int BM, int WN, bool kExact>
 static void launch_panel(GemmArgs g, hipStream_t st) {
     g.panel_rows = panel_rows(g.m, g.n, BM, 4 * WN);
     const int64_t npan = (g.n + g.panel_rows - 1) / g.panel_rows, nmt = (g.m + BM - 1) / BM;
-    panel_kernel<BM, WN, kExact><<<dim3((unsigned)(8 * nmt * ((npan + 7) / 8))), dim3(256), 0, st>>>(g);
+    const dim3 grid((unsigned)(8 * nmt * ((npan + 7) / 8)));
+    bool deep = false;
+    if constexpr (!kExact) deep = ((g.k + 127) / 128) % 4 == 0;
+    if constexpr (!kExact) {
+        if (deep) panel_kernel<BM, WN, false, 4><<<grid, dim3(256), 0, st>>>(g);
+    }
+    if (!deep) panel_kernel<BM, WN, kExact, 2><<<grid, dim3(256), 0, st>>>(g);
     count_launch(kExact ? Kern::kPanel64x128Exact : Kern::kPanel64x128, g.m);
 }
 
