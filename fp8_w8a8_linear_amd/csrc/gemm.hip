@@ -10,7 +10,7 @@
 //  * panel kernel (m up to 640 where the ring tiles are too few to fill the chip; 64 x 128
 //    tiles, or narrower weight panels where those fill the chip better): a workgroup owns a
 //    panel of up to BN weight rows and a BM-row tile of the activations. Each of its 4 waves streams
-//    its own WN weight rows straight from memory into MFMA registers, two k-steps
+//    its own WN weight rows straight from memory into MFMA registers, two or four k-steps
 //    ahead; only the activation tile, which all 4 waves share, is staged in LDS
 //    (three buffers: the operands of step k+1 are read while the MFMAs of step k
 //    run, one barrier per step). Workgroups that share a weight panel are placed on
