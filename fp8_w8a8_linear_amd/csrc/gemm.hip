@@ -112,7 +112,6 @@ __device__ __forceinline__ v4f mfma16_step(const v8i& a, const v8i& b, const v4f
 
 // ---------------------------------------------------------------- panel kernel
 
-
 __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t off) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
@@ -878,12 +877,14 @@ static void launch_panel(GemmArgs g, hipStream_t st) {
     g.panel_rows = panel_rows(g.m, g.n, BM, 4 * WN);
     const int64_t npan = (g.n + g.panel_rows - 1) / g.panel_rows, nmt = (g.m + BM - 1) / BM;
     const dim3 grid((unsigned)(8 * nmt * ((npan + 7) / 8)));
-    bool deep = false;
-    if constexpr (!kExact) deep = ((g.k + 127) / 128) % 4 == 0;
     if constexpr (!kExact) {
-        if (deep) panel_kernel<BM, WN, false, 4><<<grid, dim3(256), 0, st>>>(g);
+        if ((g.k + 127) / 128 % 4 == 0) {   // k-steps: a whole number of four-step groups
+            panel_kernel<BM, WN, false, 4><<<grid, dim3(256), 0, st>>>(g);
+            count_launch(Kern::kPanel64x128, g.m);
+            return;
+        }
     }
-    if (!deep) panel_kernel<BM, WN, kExact, 2><<<grid, dim3(256), 0, st>>>(g);
+    panel_kernel<BM, WN, kExact, 2><<<grid, dim3(256), 0, st>>>(g);
     count_launch(kExact ? Kern::kPanel64x128Exact : Kern::kPanel64x128, g.m);
 }
 
